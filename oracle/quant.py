@@ -1,0 +1,117 @@
+"""Weight / activation quantization, index packing and the dequantized
+product, fp64 oracle.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+Method ("OrbitQuant: data-agnostic quantization for image and video",
+rcap.io summary, offline and online pseudo-code):
+
+* weights, offline: W_rot = W @ R.T, row norms n, indices of the nearest
+  centroid of W_rot / n in ``codebook[d, b_w]``; W_hat = diag(n) C[idx];
+* activations, per token: x_rot = x @ R.T, s = ||x_rot||, indices of the
+  nearest centroid of x_rot / (s + eps) in ``codebook[d, b_a]``;
+  x_hat = s C[idx];
+* the rotation cancels inside the layer (W R^T R x = W x, same page,
+  "rotation cancels" paragraph), so the layer output is computed in the
+  rotated basis: y = W_hat x_hat.  The page reports the product itself as
+  a dequantize-then-matmul ("fake quantization", caveats paragraph); the
+  oracle computes exactly that product in fp64.
+
+Readings:
+
+* nearest centroid = count of thresholds strictly below u, thresholds being
+  midpoints of adjacent centroids; a tie u == theta_j takes the lower
+  centroid (the first index of argmin |u - c|).
+* eps = 1e-12 (unvalued on the page), added to the norm; the stored scale
+  is s itself.  The same guard divides weight rows by (n + eps).
+* the codebook is for d = d_in (one codebook per input dimension), not h.
+* index 0 is the most negative centroid; packing is row-major, K-contiguous,
+  least-significant bits first within each byte (2, 4 or 8 bits).
+* GELU for the MLP chain is the exact erf form, 0.5 y (1 + erf(y / sqrt 2)).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+from scipy import special
+
+from .rpbh import rotate
+
+EPS = 1e-12
+
+
+def nearest_index(u: np.ndarray, thresholds: np.ndarray) -> np.ndarray:
+    """idx = #{j : theta_j < u} (searchsorted with side='left' is that count)."""
+    return np.searchsorted(np.asarray(thresholds, dtype=np.float64), u, side="left").astype(np.int64)
+
+
+def quantize_activations(X, perm, sign, h, thresholds, eps: float = EPS):
+    """Online step per token: returns (idx[T, d], s[T], x_rot[T, d], u[T, d])."""
+    x_rot = rotate(X, perm, sign, h)
+    s = np.linalg.norm(x_rot, axis=1)
+    u = x_rot / (s + eps)[:, None]
+    return nearest_index(u, thresholds), s, x_rot, u
+
+
+def quantize_weights(W, perm, sign, h, thresholds, eps: float = EPS):
+    """Offline step per weight matrix: returns (idx[N, d], norms[N], W_rot, u)."""
+    w_rot = rotate(W, perm, sign, h)
+    n = np.linalg.norm(w_rot, axis=1)
+    u = w_rot / (n + eps)[:, None]
+    return nearest_index(u, thresholds), n, w_rot, u
+
+
+def pack(idx: np.ndarray, bits: int) -> np.ndarray:
+    """Pack [R, K] indices (< 2^bits) into [R, K*bits/8] bytes, LSB first."""
+    idx = np.asarray(idx, dtype=np.int64)
+    R, K = idx.shape
+    per = 8 // bits
+    if K % per:
+        raise ValueError("K must fill whole bytes")
+    g = idx.reshape(R, K // per, per)
+    out = np.zeros((R, K // per), dtype=np.int64)
+    for k in range(per):
+        out |= g[:, :, k] << (k * bits)
+    return out.astype(np.uint8)
+
+
+def unpack(packed: np.ndarray, bits: int, K: int) -> np.ndarray:
+    """Inverse of :func:`pack`."""
+    p = np.asarray(packed, dtype=np.int64)
+    per = 8 // bits
+    mask = (1 << bits) - 1
+    out = np.stack([(p >> (k * bits)) & mask for k in range(per)], axis=-1)
+    return out.reshape(p.shape[0], -1)[:, :K]
+
+
+def gelu_erf(y):
+    y = np.asarray(y, dtype=np.float64)
+    return 0.5 * y * (1.0 + special.erf(y / np.sqrt(2.0)))
+
+
+def dequantized_product(ia, s, iw, n, c_a, c_w, bias=None, gelu: bool = False):
+    """y = (s * C_a[ia]) @ (n * C_w[iw]).T (+ bias) (GELU), in fp64.
+
+    ia[T, K], s[T] give x_hat; iw[N, K], n[N] give W_hat (both in the rotated
+    basis, where the rotation has cancelled).
+    """
+    x_hat = np.asarray(s, dtype=np.float64)[:, None] * np.asarray(c_a, dtype=np.float64)[ia]
+    w_hat = np.asarray(n, dtype=np.float64)[:, None] * np.asarray(c_w, dtype=np.float64)[iw]
+    y = x_hat @ w_hat.T
+    if bias is not None:
+        y = y + np.asarray(bias, dtype=np.float64)[None, :]
+    if gelu:
+        y = gelu_erf(y)
+    return y
+
+
+def boundary_distance(u: np.ndarray, thresholds: np.ndarray):
+    """For each u: (|u - theta*|, theta*) for the threshold theta* nearest u."""
+    th = np.asarray(thresholds, dtype=np.float64)
+    j = np.searchsorted(th, u, side="left")
+    lo = th[np.clip(j - 1, 0, len(th) - 1)]
+    hi = th[np.clip(j, 0, len(th) - 1)]
+    dlo = np.abs(u - lo)
+    dhi = np.abs(u - hi)
+    near = np.where(dlo <= dhi, lo, hi)
+    return np.minimum(dlo, dhi), near
