@@ -1,0 +1,179 @@
+#!/usr/bin/env python
+"""Benchmark of the OrbitQuant quantized linear on one MI355X.
+
+One step = the whole hot path on one batch: rotate-and-quantize of the
+token activations (oq_rotate_quantize_act) followed by the codebook GEMM
+(oq_qlinear), on the FLUX.1-like double-stream QKV linear (4608 tokens,
+3072 -> 9216, W4A4, h = 256).  Weights are quantized once, offline,
+before timing.  Inputs are resident in HBM when the timed region starts;
+the activation batches rotate through a ring of buffers larger than the
+256 MB Infinity Cache so the rotate-quantize kernel reads from HBM.
+
+Prints one JSON line.  Per-kernel durations come from HIP events recorded
+on the launch stream around every kernel of the timed steps.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, TFLOP/s
+
+
+def cpu_baseline(lin, x, Wm, perm, sign, c_a, th_a, c_w, th_w, target_s: float = 12.0):
+    """The fp64 oracle on the host cores, on a bounded sample of tokens of the
+    same workload, in the same unit as the GPU value (TFLOP/s of the layer)."""
+    import numpy as np
+    from oracle import quant
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    # offline weight step (not timed, as on the GPU)
+    iw, n_w, _, _ = quant.quantize_weights(Wm.astype(np.float64), perm, sign, lin.h, th_w)
+
+    def run(n):
+        xs = x[:n].astype(np.float64)
+        t0 = time.perf_counter()
+        ia, s, _, _ = quant.quantize_activations(xs, perm, sign, lin.h, th_a)
+        quant.dequantized_product(ia, s, iw, n_w, c_a, c_w)
+        return time.perf_counter() - t0
+
+    t_probe = run(32)
+    n = int(min(lin.T, max(32, 32 * target_s / max(t_probe, 1e-3))))
+    t = run(n)
+    flops = 2.0 * n * lin.d_in * lin.d_out
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} of {lin.T} tokens (rotate-quantize + fp64 dequantized product), {t:.1f} s",
+            "tokens_per_s": n / t}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="flux_qkv_w4a4")
+    ap.add_argument("--ring-mb", type=float, default=640.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (the layer is "
+              "token-parallel; see the sharding design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from free_bit_quantization_amd import oq, synth
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    wl = synth.workloads()[args.workload]
+    lin = wl.linears[0]
+    T, K, N, h = lin.T, lin.d_in, lin.d_out, lin.h
+    x, Wm = synth.gen_linear(lin, 0, 0)
+    perm, sign = oq.oq_build_rpbh(K, h, 0)
+    c_a, th_a, _ = oq.oq_lloyd_max(K, lin.bits_a)
+    c_w, th_w, _ = oq.oq_lloyd_max(K, lin.bits_w)
+    pd = torch.from_numpy(perm).to(dev)
+    sd = torch.from_numpy(sign).to(dev)
+    xt = torch.from_numpy(x).to(dev)
+    if lin.act_dtype == "bf16":
+        xt = xt.to(torch.bfloat16)
+    Wd = torch.from_numpy(Wm).to(dev)
+    w_idx, w_norm = oq.oq_quantize_weights(Wd, h, pd, sd, th_w, lin.bits_w)
+    del Wd
+
+    # ring of activation batches (distinct buffers) larger than the Infinity Cache
+    nring = max(1, math.ceil(args.ring_mb * 1e6 / (xt.numel() * xt.element_size())))
+    ring = [torch.roll(xt, shifts=i * 7, dims=0).contiguous() for i in range(nring)]
+    x_idx = torch.empty((T, K * lin.bits_a // 8), dtype=torch.uint8, device=dev)
+    s = torch.empty(T, dtype=torch.float32, device=dev)
+    y = torch.empty((T, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        oq.oq_rotate_quantize_act(ring[i % nring], h, pd, sd, th_a, lin.bits_a, x_idx=x_idx, s=s, stream=stream)
+        oq.oq_qlinear(x_idx, s, w_idx, w_norm, K, c_a, lin.bits_a, c_w, lin.bits_w, y=y, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        e = ev[i]
+        e[0].record(stream)
+        oq.oq_rotate_quantize_act(ring[i % nring], h, pd, sd, th_a, lin.bits_a, x_idx=x_idx, s=s, stream=stream)
+        e[1].record(stream)
+        oq.oq_qlinear(x_idx, s, w_idx, w_norm, K, c_a, lin.bits_a, c_w, lin.bits_w, y=y, stream=stream)
+        e[2].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+
+    total_ms = start.elapsed_time(end)
+    ms_step = total_ms / args.steps
+    t_rq = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
+    t_ql = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
+
+    es = xt.element_size()
+    rq_bytes = T * K * es + T * K * lin.bits_a // 8 + 4 * T       # read x, write indices and s
+    flops = 2.0 * T * K * N
+    rq_gbs = rq_bytes / (t_rq * 1e-3) / 1e9
+    ql_tflops = flops / (t_ql * 1e-3) / 1e12
+    value = flops / (ms_step * 1e-3) / 1e12
+
+    line = {
+        "metric": "qlinear TFLOP/s + rotate-quant GB/s (frac of roofline), FLUX 3072-wide W4A4",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16-mfma/fp32-acc; fp32 rotate",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {T} tokens, {K}->{N}, W{lin.bits_w}A{lin.bits_a}, h={h}, "
+                               f"{lin.act_dtype} activations", "tokens": T, "d_in": K, "d_out": N, "h": h,
+                   "bits_w": lin.bits_w, "bits_a": lin.bits_a, "activation_ring_buffers": nring},
+        "tokens_per_s": round(T / (ms_step * 1e-3), 1),
+        "qlinear_TFLOPs": round(ql_tflops, 2),
+        "qlinear_ms": round(t_ql, 5),
+        "rotate_quant_GBps": round(rq_gbs, 1),
+        "rotate_quant_ms": round(t_rq, 5),
+        "roofline": {"bound": "mfma", "achieved": round(ql_tflops, 2), "peak": FP16_MFMA_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(ql_tflops / FP16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "oq_qlinear (ql_kernel<4,4>)", "algorithmic": f"2*T*K*N = {flops:.4g} flop"},
+        "roofline_rotate_quant": {"bound": "hbm", "achieved": round(rq_gbs, 1), "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": round(rq_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                                  "kernel": "oq_rotate_quantize_act (rq_act_kernel<8,bf16,4>)",
+                                  "algorithmic": f"T*(K*{es} + K*{lin.bits_a}/8 + 4) = {rq_bytes} B"},
+        "wall_s_timed": round(t_wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(lin, x, Wm, perm, sign, c_a, th_a, c_w, th_w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

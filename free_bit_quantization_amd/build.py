@@ -1,0 +1,56 @@
+"""Build liboq.so (the HIP library behind the C ABI in include/oq.h) for gfx950.
+
+Every source is compiled by hipcc for gfx950 only, with the packed-fp32
+instruction feature switched off, and linked in-tree next to this file.
+"""
+
+from __future__ import annotations
+
+import concurrent.futures
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(HERE, "liboq.so")
+SOURCES = ["api.cpp", "host_rpbh.cpp", "host_lloyd_max.cpp", "rotate_quantize.hip", "qlinear.hip"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+ARCH = "gfx950"
+FLAGS = ["-x", "hip", f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Wno-unused-result", f"-I{INCLUDE}", f"-I{CSRC}"]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("build failed:\n" + " ".join(cmd) + "\n" + r.stdout[-8000:])
+    return r.stdout
+
+
+def build(verbose: bool = False, jobs: int = 0) -> str:
+    """Compile and link liboq.so; returns its path.  Always recompiles."""
+    os.makedirs(BUILD, exist_ok=True)
+    objs = []
+    cmds = []
+    for src in SOURCES:
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        objs.append(obj)
+        cmds.append([HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj])
+    jobs = jobs or min(len(cmds), max(1, (os.cpu_count() or 2)))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        for out in ex.map(_run, cmds):
+            if verbose and out.strip():
+                print(out)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

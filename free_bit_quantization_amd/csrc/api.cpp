@@ -1,0 +1,199 @@
+// C ABI of liboq: argument validation, launch planning, error reporting.
+// Every entry point validates all arguments before launching anything; an
+// invalid argument returns OQ_EINVAL with no side effect.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "oq_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+oq_status fail(oq_status code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+oq_status ok() {
+  g_err[0] = 0;
+  return OQ_OK;
+}
+
+oq_status device_error(hipError_t e, const char* what) {
+  return fail(OQ_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+int log2_exact(int32_t h) {
+  if (h < 2 || (h & (h - 1)) != 0) return -1;
+  int m = 0;
+  while ((1 << m) < h) ++m;
+  return m;
+}
+
+bool bits_ok(int32_t b) { return b == 2 || b == 4 || b == 8; }
+
+// Thresholds must be finite and strictly increasing, also after rounding to fp32.
+oq_status check_thresholds(const double* th, int n, bool need_f32) {
+  if (!th) return fail(OQ_EINVAL, "thresholds is NULL");
+  for (int i = 0; i < n; ++i) {
+    if (!std::isfinite(th[i])) return fail(OQ_EINVAL, "threshold %d is not finite", i);
+    if (i > 0 && !(th[i] > th[i - 1])) return fail(OQ_EINVAL, "thresholds not strictly increasing at %d", i);
+    if (need_f32 && i > 0 && !((float)th[i] > (float)th[i - 1]))
+      return fail(OQ_EINVAL, "thresholds %d and %d coincide in fp32", i - 1, i);
+  }
+  return OQ_OK;
+}
+
+uint16_t to_f16_bits(double v) {
+  const _Float16 h = (_Float16)v;
+  uint16_t b;
+  std::memcpy(&b, &h, 2);
+  return b;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* oq_last_error(void) { return g_err; }
+
+const char* oq_version(void) { return "liboq 0.1 (gfx950)"; }
+
+oq_status oq_build_rpbh(int32_t d, int32_t h, uint64_t seed, int32_t* perm, int8_t* sign) {
+  if (d < 2) return fail(OQ_EINVAL, "d must be >= 2 (got %d)", d);
+  if (log2_exact(h) < 0) return fail(OQ_EINVAL, "h must be a power of two >= 2 (got %d)", h);
+  if (d % h != 0) return fail(OQ_EINVAL, "h (%d) must divide d (%d)", h, d);
+  if (!perm || !sign) return fail(OQ_EINVAL, "perm / sign is NULL");
+  oq::build_rpbh_tables(d, seed, perm, sign);
+  return ok();
+}
+
+oq_status oq_lloyd_max(int32_t d, int32_t bits, double* centroids, double* thresholds, double* mse) {
+  if (d < 3) return fail(OQ_EINVAL, "d must be >= 3 (got %d)", d);
+  if (bits < 1 || bits > 8) return fail(OQ_EINVAL, "bits must be in 1..8 (got %d)", bits);
+  if (!centroids || !thresholds) return fail(OQ_EINVAL, "centroids / thresholds is NULL");
+  double resid = 0.0;
+  if (oq::lloyd_max_fd(d, bits, centroids, thresholds, mse, &resid) != 0)
+    return fail(OQ_ENOCONV, "Lloyd-Max residual %.3g above 1e-10 (d=%d, bits=%d)", resid, d, bits);
+  return ok();
+}
+
+oq_status oq_quantize_weights(const void* W, oq_dtype w_dtype, int32_t d_out, int32_t d_in, int32_t h,
+                              const int32_t* perm, const int8_t* sign, const double* thresholds, int32_t bits_w,
+                              uint8_t* w_idx, float* w_norm, hipStream_t stream) {
+  const int m = log2_exact(h);
+  if (w_dtype != OQ_F32 && w_dtype != OQ_BF16) return fail(OQ_EINVAL, "w_dtype must be OQ_F32 or OQ_BF16");
+  if (d_out < 0) return fail(OQ_EINVAL, "d_out must be >= 0");
+  if (d_in < 2 || m < 0 || d_in % h != 0) return fail(OQ_EINVAL, "need h a power of two >= 2 dividing d_in");
+  if (!bits_ok(bits_w)) return fail(OQ_EINVAL, "bits_w must be 2, 4 or 8 (got %d)", bits_w);
+  if ((d_in * bits_w) % 8 != 0) return fail(OQ_EINVAL, "d_in * bits_w must fill whole bytes");
+  const int nthr = (1 << bits_w) - 1;
+  oq_status st = check_thresholds(thresholds, nthr, false);
+  if (st != OQ_OK) return st;
+  if (d_out > 0 && (!W || !perm || !sign || !w_idx || !w_norm)) return fail(OQ_EINVAL, "NULL device pointer");
+  if (h > 256) return fail(OQ_EUNSUPPORTED, "h > 256 has no kernel");
+  if ((size_t)d_in * 8 + 256 * 8 + 64 > 160 * 1024) return fail(OQ_EUNSUPPORTED, "d_in %d too large for the LDS row", d_in);
+  if (d_out == 0) return ok();
+  oq::WqArgs a{};
+  a.W = W; a.d_out = d_out; a.d = d_in; a.h = h; a.perm = perm; a.sign = sign;
+  a.w_idx = w_idx; a.w_norm = w_norm; a.nthr = nthr;
+  for (int i = 0; i < nthr; ++i) a.thr[i] = thresholds[i];
+  hipError_t e = oq::wq_launch(a, w_dtype == OQ_BF16, bits_w, stream);
+  if (e != hipSuccess) return device_error(e, "oq_quantize_weights launch");
+  return ok();
+}
+
+oq_status oq_rotate_quantize_act(const void* x, oq_dtype x_dtype, int64_t T, int32_t d, int32_t h,
+                                 const int32_t* perm, const int8_t* sign, const double* thresholds, int32_t bits_a,
+                                 uint8_t* x_idx, float* s, float* x_rot, hipStream_t stream) {
+  const int m = log2_exact(h);
+  if (x_dtype != OQ_F32 && x_dtype != OQ_BF16) return fail(OQ_EINVAL, "x_dtype must be OQ_F32 or OQ_BF16");
+  if (T < 0) return fail(OQ_EINVAL, "T must be >= 0");
+  if (d < 16 || d % 16 != 0) return fail(OQ_EINVAL, "d must be a positive multiple of 16 (got %d)", d);
+  if (m < 0 || d % h != 0) return fail(OQ_EINVAL, "need h a power of two >= 2 dividing d");
+  if (!bits_ok(bits_a)) return fail(OQ_EINVAL, "bits_a must be 2, 4 or 8 (got %d)", bits_a);
+  const int nthr = (1 << bits_a) - 1;
+  oq_status st = check_thresholds(thresholds, nthr, true);
+  if (st != OQ_OK) return st;
+  if (T > 0 && (!x || !perm || !sign || !x_idx || !s)) return fail(OQ_EINVAL, "NULL device pointer");
+  if (m > 8) return fail(OQ_EUNSUPPORTED, "h > 256 has no kernel");
+
+  // Threshold-search grid: cells of width w over [theta_0, theta_{L-2}], each
+  // widened by 0.02 w (rounding of the cell index) and by the largest guard
+  // radius, must hold at most one threshold.
+  float th32[oq::kMaxThr];
+  for (int i = 0; i < nthr; ++i) th32[i] = (float)thresholds[i];
+  const double lo = th32[0], hi = th32[nthr - 1];
+  double min_gap = INFINITY;
+  for (int i = 1; i < nthr; ++i) min_gap = std::fmin(min_gap, (double)th32[i] - (double)th32[i - 1]);
+  const double rmax = (2.0 * m + 24.0) * std::ldexp(1.0, -24);
+  int G = 0;
+  if (hi > lo) {
+    const double wmax = (min_gap - 2.2 * rmax) / 1.1;
+    if (wmax > 0) {
+      const double need = (hi - lo) / wmax;
+      int g = 1;
+      while (g < need && g <= oq::kMaxGrid) g <<= 1;
+      if (g <= oq::kMaxGrid) G = g;
+    }
+  }
+  oq::RqPlan plan;
+  if (!oq::rq_plan(d, m, x_dtype == OQ_BF16, T, G, &plan))
+    return fail(OQ_EUNSUPPORTED, "no rotate-quantize kernel for d=%d h=%d (d/16 must be a multiple of 64 up to 768, or a power of two below 64)", d, h);
+  if (T == 0) return ok();
+
+  oq::RqArgs a{};
+  a.x = x; a.T = T; a.d = d; a.log2h = m; a.perm = perm; a.sign = sign;
+  a.x_idx = x_idx; a.s = s; a.x_rot = x_rot; a.nthr = nthr; a.G = G;
+  a.g_lo = lo;
+  a.g_invw = G > 0 ? G / (hi - lo) : 0.0;
+  a.g_rmax = rmax;
+  for (int i = 0; i < nthr; ++i) a.thr[i] = th32[i];
+  hipError_t e = oq::rq_launch(a, x_dtype == OQ_BF16, bits_a, plan, stream);
+  if (e != hipSuccess) return device_error(e, "oq_rotate_quantize_act launch");
+  return ok();
+}
+
+oq_status oq_qlinear(const uint8_t* x_idx, const float* s, int64_t T, const uint8_t* w_idx, const float* w_norm,
+                     int32_t d_out, int32_t d_in, const double* centroids_a, int32_t bits_a,
+                     const double* centroids_w, int32_t bits_w, const float* bias, int32_t epilogue, float* y,
+                     hipStream_t stream) {
+  if (T < 0 || d_out < 0) return fail(OQ_EINVAL, "T and d_out must be >= 0");
+  if (d_in <= 0) return fail(OQ_EINVAL, "d_in must be > 0");
+  if (!bits_ok(bits_a) || !bits_ok(bits_w)) return fail(OQ_EINVAL, "bits must be 2, 4 or 8");
+  if (epilogue != OQ_EPI_NONE && epilogue != OQ_EPI_GELU_ERF) return fail(OQ_EINVAL, "unknown epilogue %d", epilogue);
+  if (!centroids_a || !centroids_w) return fail(OQ_EINVAL, "centroids is NULL");
+  const int La = 1 << bits_a, Lw = 1 << bits_w;
+  for (int i = 0; i < La; ++i)
+    if (!std::isfinite(centroids_a[i])) return fail(OQ_EINVAL, "centroids_a[%d] not finite", i);
+  for (int i = 0; i < Lw; ++i)
+    if (!std::isfinite(centroids_w[i])) return fail(OQ_EINVAL, "centroids_w[%d] not finite", i);
+  if (T > 0 && d_out > 0 && (!x_idx || !s || !w_idx || !w_norm || !y)) return fail(OQ_EINVAL, "NULL device pointer");
+  if (d_in % 64 != 0) return fail(OQ_EUNSUPPORTED, "d_in must be a multiple of 64 (got %d)", d_in);
+  if (!((bits_a == 4 || bits_a == 8) && (bits_w == 2 || bits_w == 4)))
+    return fail(OQ_EUNSUPPORTED, "no GEMM kernel for W%dA%d", bits_w, bits_a);
+  const double sk = std::sqrt((double)d_in);
+  for (int i = 0; i < La; ++i)
+    if (std::fabs(sk * centroids_a[i]) > 60000.0) return fail(OQ_EINVAL, "sqrt(d_in)*centroids_a exceeds fp16");
+  for (int i = 0; i < Lw; ++i)
+    if (std::fabs(sk * centroids_w[i]) > 60000.0) return fail(OQ_EINVAL, "sqrt(d_in)*centroids_w exceeds fp16");
+  if (T == 0 || d_out == 0) return ok();
+
+  oq::QlArgs a{};
+  a.x_idx = x_idx; a.s = s; a.T = T; a.w_idx = w_idx; a.w_norm = w_norm;
+  a.N = d_out; a.K = d_in; a.bias = bias; a.y = y; a.epilogue = epilogue;
+  a.scale = (float)(1.0 / d_in);
+  for (int i = 0; i < 256; ++i) a.tab_a[i] = i < La ? to_f16_bits(sk * centroids_a[i]) : 0;
+  for (int i = 0; i < 256; ++i) a.tab_w[i] = i < Lw ? to_f16_bits(sk * centroids_w[i]) : 0;
+  hipError_t e = oq::ql_launch(a, bits_a, bits_w, stream);
+  if (e != hipSuccess) return device_error(e, "oq_qlinear launch");
+  return ok();
+}
+
+}  // extern "C"

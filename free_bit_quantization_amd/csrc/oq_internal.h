@@ -1,0 +1,87 @@
+// Internal declarations shared by the C-ABI layer and the HIP kernels.
+#ifndef OQ_INTERNAL_H_
+#define OQ_INTERNAL_H_
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+#include "oq.h"
+
+namespace oq {
+
+// ---- host math --------------------------------------------------------------
+void build_rpbh_tables(int32_t d, uint64_t seed, int32_t* perm, int8_t* sign);
+// 0 on convergence (relative fixed-point residual <= 1e-10), -1 otherwise.
+int lloyd_max_fd(int d, int bits, double* centroids, double* thresholds, double* mse, double* resid);
+
+// ---- rotate-quantize (activations, fp32 fast path + fp64 recheck) ------------
+constexpr int kMaxThr = 255;     // 2^8 - 1 thresholds
+constexpr int kMaxGrid = 4096;   // cells of the threshold-search grid
+
+struct RqArgs {
+  const void* x;
+  int64_t T;
+  int32_t d;
+  int32_t log2h;
+  const int32_t* perm;
+  const int8_t* sign;
+  uint8_t* x_idx;
+  float* s;
+  float* x_rot;
+  int32_t nthr;      // 2^bits - 1
+  int32_t G;         // grid cells (power of two), 0 = binary search
+  double g_lo;       // grid origin (u units)
+  double g_invw;     // cells per unit u
+  double g_rmax;     // widening of each cell for the recheck guard (u units)
+  float thr[kMaxThr];
+};
+
+// Plan of a launch, chosen on the host from (d, h, dtype, bits, T).
+struct RqPlan {
+  int ns;        // slots (16 coordinates each) per token
+  int tpw;       // tokens per workgroup iteration
+  int threads;   // workgroup size
+  int grid;      // workgroups
+  size_t lds;    // dynamic LDS bytes
+};
+
+// Returns false if (d, h) has no kernel.
+bool rq_plan(int32_t d, int32_t log2h, bool bf16, int64_t T, int G, RqPlan* plan);
+hipError_t rq_launch(const RqArgs& a, bool bf16, int bits, const RqPlan& plan, hipStream_t stream);
+
+// ---- weight quantization (offline, fp64) --------------------------------------
+struct WqArgs {
+  const void* W;
+  int32_t d_out;
+  int32_t d;
+  int32_t h;
+  const int32_t* perm;
+  const int8_t* sign;
+  uint8_t* w_idx;
+  float* w_norm;
+  int32_t nthr;
+  double thr[kMaxThr];
+};
+hipError_t wq_launch(const WqArgs& a, bool bf16, int bits, hipStream_t stream);
+
+// ---- codebook GEMM ------------------------------------------------------------
+struct QlArgs {
+  const uint8_t* x_idx;
+  const float* s;
+  int64_t T;
+  const uint8_t* w_idx;
+  const float* w_norm;
+  int32_t N;
+  int32_t K;
+  const float* bias;
+  float* y;
+  float scale;           // 1 / K (tables hold sqrt(K) * c)
+  int32_t epilogue;
+  uint16_t tab_a[256];   // fp16 bits of sqrt(K) * c_a
+  uint16_t tab_w[256];   // fp16 bits of sqrt(K) * c_w
+};
+hipError_t ql_launch(const QlArgs& a, int bits_a, int bits_w, hipStream_t stream);
+
+}  // namespace oq
+
+#endif  // OQ_INTERNAL_H_

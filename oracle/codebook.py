@@ -155,8 +155,8 @@ def lloyd_max(dens, L: int, lloyd_steps: int = 50, newton_steps: int = 200, tol:
     # compander start: quantiles of N(0, 3 sigma^2) at (j + 1/2)/L
     p = (np.arange(L) + 0.5) / L
     c = math.sqrt(3.0) * dens.sigma * special.ndtri(p)
-    if np.isfinite(dens.hi):
-        c = np.clip(c, 0.999 * dens.lo, 0.999 * dens.hi)
+    if np.isfinite(dens.hi) and np.max(np.abs(c)) > 0.95 * dens.hi:
+        c *= 0.95 * dens.hi / np.max(np.abs(c))    # keep the start inside a bounded support
     c = 0.5 * (c - c[::-1])
 
     for _ in range(lloyd_steps):

@@ -1,0 +1,155 @@
+"""Shared helpers of the GPU parity tests: run one linear through liboq and
+through the fp64 oracle on the same seeded inputs and compare."""
+
+from __future__ import annotations
+
+import dataclasses
+import sys
+from typing import Optional
+
+import numpy as np
+
+from free_bit_quantization_amd import oq, synth
+from oracle import codebook, quant, rpbh
+
+REL_XROT = 1e-5       # per-token relative L2 of the rotated activations
+REL_S = 1e-5          # relative error of the token norms
+REL_GEMM = 2e-3       # relative Frobenius error of the GEMM output
+BAND = 1e-6           # indices may differ only within BAND * |theta| of a threshold
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@dataclasses.dataclass
+class Codebooks:
+    c: np.ndarray
+    th: np.ndarray
+
+
+_cb_cache = {}
+
+
+def library_codebook(d: int, bits: int) -> Codebooks:
+    """The library's codebook, checked against the oracle's own Lloyd-Max solve."""
+    key = (d, bits)
+    if key not in _cb_cache:
+        c, th, _ = oq.oq_lloyd_max(d, bits)
+        co, _, _, _ = codebook.lloyd_max_fd(d, bits)
+        assert np.max(np.abs(c - co)) <= 1e-6 * np.max(np.abs(co))
+        _cb_cache[key] = Codebooks(c, th)
+    return _cb_cache[key]
+
+
+def index_mismatches(gpu_idx: np.ndarray, ora_idx: np.ndarray, u: np.ndarray, th: np.ndarray):
+    """(total mismatches, in-band, out-of-band): a mismatch is in band if the
+    oracle's u lies within BAND * |theta| of a threshold between the two choices."""
+    mis = np.nonzero(gpu_idx != ora_idx)
+    n = len(mis[0])
+    if n == 0:
+        return 0, 0, 0
+    g = gpu_idx[mis]
+    o = ora_idx[mis]
+    uu = u[mis]
+    inband = 0
+    for gi, oi, ui in zip(g, o, uu):
+        lo, hi = min(gi, oi), max(gi, oi)
+        # thresholds separating the two choices: theta_lo .. theta_{hi-1}
+        ths = th[lo:hi]
+        if hi - lo == 1 and abs(ui - ths[0]) <= BAND * abs(ths[0]):
+            inband += 1
+    return n, inband, n - inband
+
+
+def rel_frob(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def to_device(x: np.ndarray, dtype: str):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    if dtype == "bf16":
+        t = t.to(torch.bfloat16)       # exact: values are already bf16-representable
+    return t.cuda()
+
+
+def rotation(d: int, h: int, seed: int = 0):
+    import torch
+    perm, sign = oq.oq_build_rpbh(d, h, seed)
+    po, so = rpbh.build_rpbh(d, h, seed)
+    assert np.array_equal(perm, po) and np.array_equal(sign, so)
+    return perm, sign, torch.from_numpy(perm).cuda(), torch.from_numpy(sign).cuda()
+
+
+def check_activations(x: np.ndarray, dtype: str, h: int, bits: int, seed: int = 0, rows: Optional[np.ndarray] = None,
+                      want_x_rot: bool = True, name: str = ""):
+    """rotate-quantize x on the GPU; compare rows (all if None) with the oracle.
+
+    Returns (x_idx device tensor, s device tensor, report dict)."""
+    T, d = x.shape
+    perm, sign, pd, sd = rotation(d, h, seed)
+    cb = library_codebook(d, bits)
+    xd = to_device(x, dtype)
+    x_idx, s, x_rot = oq.oq_rotate_quantize_act(xd, h, pd, sd, cb.th, bits, want_x_rot=want_x_rot)
+    import torch
+    torch.cuda.synchronize()
+    rows = np.arange(T) if rows is None else rows
+    xs = np.asarray(xd.float().cpu().numpy(), dtype=np.float64)[rows]
+    ia, s_o, xr_o, u_o = quant.quantize_activations(xs, perm, sign, h, cb.th)
+    gi = quant.unpack(x_idx.cpu().numpy()[rows], bits, d)
+    n, nin, nout = index_mismatches(gi, ia, u_o, cb.th)
+    s_g = s.cpu().numpy()[rows].astype(np.float64)
+    rep = {"name": name, "T": T, "d": d, "h": h, "bits": bits, "checked_rows": len(rows),
+           "idx_mismatch": n, "idx_in_band": nin, "idx_out_of_band": nout,
+           "s_rel": float(np.max(np.abs(s_g - s_o) / np.maximum(s_o, 1e-30)))}
+    if want_x_rot:
+        xr_g = x_rot.cpu().numpy()[rows].astype(np.float64)
+        num = np.linalg.norm(xr_g - xr_o, axis=1)
+        den = np.maximum(np.linalg.norm(xr_o, axis=1), 1e-30)
+        rep["x_rot_rel"] = float(np.max(num / den))
+    log(f"[act] {rep}")
+    return x_idx, s, rep
+
+
+def check_weights(W: np.ndarray, h: int, bits: int, seed: int = 0, name: str = ""):
+    """Quantize W on the GPU (fp64 path); indices must be bit-exact."""
+    d_out, d = W.shape
+    perm, sign, pd, sd = rotation(d, h, seed)
+    cb = library_codebook(d, bits)
+    Wd = to_device(W, "f32")
+    w_idx, w_norm = oq.oq_quantize_weights(Wd, h, pd, sd, cb.th, bits)
+    iw, n_o, _, uw = quant.quantize_weights(W.astype(np.float64), perm, sign, h, cb.th)
+    gi = quant.unpack(w_idx.cpu().numpy(), bits, d)
+    n, nin, nout = index_mismatches(gi, iw, uw, cb.th)
+    nrel = float(np.max(np.abs(w_norm.cpu().numpy() - n_o) / n_o))
+    rep = {"name": name, "d_out": d_out, "d": d, "bits": bits, "idx_mismatch": n, "w_norm_rel": nrel}
+    log(f"[w] {rep}")
+    return w_idx, w_norm, rep
+
+
+def check_gemm(x_idx, s, w_idx, w_norm, d: int, bits_a: int, bits_w: int, bias=None, gelu=False,
+               rows: Optional[np.ndarray] = None, name: str = ""):
+    """GEMM on the GPU vs the oracle's dequantized product of the GPU's own indices."""
+    import torch
+    ca = library_codebook(d, bits_a)
+    cw = library_codebook(d, bits_w)
+    bd = None if bias is None else torch.from_numpy(bias).cuda()
+    y = oq.oq_qlinear(x_idx, s, w_idx, w_norm, d, ca.c, bits_a, cw.c, bits_w, bias=bd,
+                      epilogue=oq.OQ_EPI_GELU_ERF if gelu else oq.OQ_EPI_NONE)
+    torch.cuda.synchronize()
+    T = s.shape[0]
+    rows = np.arange(T) if rows is None else rows
+    ia = quant.unpack(x_idx.cpu().numpy()[rows], bits_a, d)
+    iw = quant.unpack(w_idx.cpu().numpy(), bits_w, d)
+    ref = quant.dequantized_product(ia, s.cpu().numpy()[rows], iw, w_norm.cpu().numpy(), ca.c, cw.c,
+                                    bias=bias, gelu=gelu)
+    yg = y.cpu().numpy()[rows]
+    err = rel_frob(yg, ref)
+    rep = {"name": name, "T": T, "N": w_norm.shape[0], "K": d, "checked_rows": len(rows), "rel_frob": err,
+           "finite": bool(np.all(np.isfinite(yg)))}
+    log(f"[gemm] {rep}")
+    return y, rep

@@ -1,0 +1,192 @@
+"""GPU parity: liboq's kernels against the fp64 oracle on the same seeded
+inputs, through the C ABI (Python binding = marshalling only).
+
+Bars: packed indices bit-exact except within 1e-6 |theta| of a threshold
+(weights: bit-exact); rotated activations and norms within 1e-5 relative;
+GEMM within 2e-3 relative Frobenius of the oracle's dequantized product of
+the GPU's own indices, norms and scales."""
+
+import numpy as np
+import pytest
+
+import _parity as P
+from free_bit_quantization_amd import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+W = synth.workloads()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.set_device(0)
+
+
+def _assert_act(rep):
+    assert rep["idx_out_of_band"] == 0, rep
+    assert rep["s_rel"] <= P.REL_S, rep
+    if "x_rot_rel" in rep:
+        assert rep["x_rot_rel"] <= P.REL_XROT, rep
+
+
+def _assert_w(rep):
+    assert rep["idx_mismatch"] == 0, rep
+    assert rep["w_norm_rel"] <= 1e-6, rep
+
+
+def _assert_gemm(rep):
+    assert rep["finite"], rep
+    assert rep["rel_frob"] <= P.REL_GEMM, rep
+
+
+def run_linear(lin, index=0, T=None, seed=0, bias=False, act_rows=None, gemm_rows=None, x=None, W_=None,
+               x_dtype=None):
+    P.log(f"== linear {lin.name} T={T or lin.T} K={lin.d_in} N={lin.d_out} W{lin.bits_w}A{lin.bits_a}")
+    xg, Wg = synth.gen_linear(lin, seed, index, T=T, need_act=x is None)
+    x = xg if x is None else x
+    W_ = Wg if W_ is None else W_
+    x_idx, s, ra = P.check_activations(x, x_dtype or lin.act_dtype, lin.h, lin.bits_a, rows=act_rows,
+                                       want_x_rot=True, name=lin.name)
+    _assert_act(ra)
+    w_idx, w_norm, rw = P.check_weights(W_, lin.h, lin.bits_w, name=lin.name)
+    _assert_w(rw)
+    b = synth.gen_bias(lin.d_out, seed) if bias else None
+    y, rg = P.check_gemm(x_idx, s, w_idx, w_norm, lin.d_in, lin.bits_a, lin.bits_w, bias=b,
+                         gelu=lin.epilogue == "gelu", rows=gemm_rows, name=lin.name)
+    _assert_gemm(rg)
+    return y
+
+
+# ---- small and prefix workloads (oracle over every output) ------------------
+
+
+def test_single_linear_w4a4_full():
+    run_linear(W["single_w4a4_64x256x256"].linears[0])
+
+
+def test_single_linear_with_bias():
+    run_linear(W["single_w4a4_64x256x256"].linears[0], bias=True, seed=3)
+
+
+def test_flux_qkv_prefix_ragged():
+    run_linear(W["flux_qkv_w4a4"].linears[0], T=300)
+
+
+def test_flux_mlp_chain_prefix():
+    up, down = W["flux_mlp_w2a4"].linears
+    y_up = run_linear(up, index=0, T=264)
+    # the down projection takes GELU(up) in fp32, exactly as the GPU produced it
+    x_down = y_up.cpu().numpy().astype(np.float32)
+    _, W_down = synth.gen_linear(down, 0, 1, T=1, need_act=False)
+    run_linear(down, index=1, T=264, x=x_down, W_=W_down, x_dtype="f32")
+
+
+def test_wan_ffn_prefix_ragged():
+    run_linear(W["wan_ffn_w4a4"].linears[0], T=200)
+
+
+@pytest.mark.parametrize("k", range(8))
+def test_flux_block_w4a8_prefix(k):
+    lin = W["flux_block_w4a8_b2"].linears[k]
+    run_linear(lin, index=k, T=136 if lin.T > 1024 else 72)
+
+
+# ---- edge cases ----------------------------------------------------------------
+
+
+@pytest.mark.parametrize("d,h,dtype", [(256, 2, "f32"), (256, 4, "bf16"), (256, 16, "f32"), (512, 32, "bf16"),
+                                       (1024, 64, "f32"), (1024, 128, "bf16"), (2048, 256, "bf16"),
+                                       (64, 64, "f32"), (16, 16, "bf16"), (12288, 256, "f32")])
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_rotate_quantize_shapes_and_widths(d, h, dtype, bits):
+    rng = np.random.default_rng(d * 7 + h + bits)
+    T = 37
+    x = rng.standard_t(3, size=(T, d)).astype(np.float32) * np.float32(3.0)
+    if dtype == "bf16":
+        x = synth.bf16_round(x)
+    _, _, rep = P.check_activations(x, dtype, h, bits, name=f"shape d={d} h={h}")
+    _assert_act(rep)
+
+
+def test_zero_rows_single_token_and_repeatability():
+    rng = np.random.default_rng(5)
+    d, h, bits = 3072, 256, 4
+    x = synth.bf16_round(rng.standard_normal((5, d)).astype(np.float32))
+    x[1] = 0.0
+    x[3] = 0.0
+    x_idx, s, rep = P.check_activations(x, "bf16", h, bits, name="zero rows")
+    _assert_act(rep)
+    s_h = s.cpu().numpy()
+    assert s_h[1] == 0.0 and s_h[3] == 0.0
+    idx = x_idx.cpu().numpy()
+    # a zero row quantizes every coordinate to the index just below 0 (L/2 - 1)
+    assert np.all(idx[1] == (7 | (7 << 4)))
+    # one token
+    _, _, rep1 = P.check_activations(x[:1], "bf16", h, bits, name="T=1")
+    _assert_act(rep1)
+    # repeat runs give bit-identical outputs
+    xi2, s2, _ = P.check_activations(x, "bf16", h, bits, want_x_rot=False, name="repeat")
+    assert np.array_equal(xi2.cpu().numpy(), idx) and np.array_equal(s2.cpu().numpy(), s_h)
+
+
+def test_gemm_ragged_m_and_n_tails_and_bias():
+    # T and d_out not multiples of the 256 x 256 tile
+    rng = np.random.default_rng(9)
+    d, h = 1024, 256
+    lin = synth.Linear("ragged", 333, d, 300, h, 4, 4, "student_t", "bf16", 10, 30.0, 0.5, 5, 10.0)
+    run_linear(lin, bias=True)
+    del rng
+
+
+def test_gemm_gelu_epilogue_w2a4():
+    lin = synth.Linear("gelu", 130, 1024, 520, 256, 2, 4, "student_t", "bf16", 10, 30.0, 0.5, 5, 10.0, "gelu")
+    run_linear(lin, bias=True)
+
+
+def test_gemm_repeatable():
+    lin = W["single_w4a4_64x256x256"].linears[0]
+    x, Wm = synth.gen_linear(lin, 0, 0)
+    x_idx, s, _ = P.check_activations(x, "f32", lin.h, 4, want_x_rot=False)
+    w_idx, w_norm, _ = P.check_weights(Wm, lin.h, 4)
+    y1, _ = P.check_gemm(x_idx, s, w_idx, w_norm, lin.d_in, 4, 4)
+    y2, _ = P.check_gemm(x_idx, s, w_idx, w_norm, lin.d_in, 4, 4)
+    assert torch.equal(y1, y2)
+
+
+# ---- full sizes, sampled outputs ------------------------------------------------
+
+
+def _sample_rows(T, n, seed=0):
+    rng = np.random.default_rng(seed)
+    head = np.arange(min(16, T))
+    tail = np.arange(max(0, T - 16), T)
+    mid = rng.choice(T, size=min(n, T), replace=False)
+    return np.unique(np.concatenate([head, mid, tail]))
+
+
+def test_full_flux_qkv_w4a4():
+    lin = W["flux_qkv_w4a4"].linears[0]
+    run_linear(lin, act_rows=None, gemm_rows=_sample_rows(lin.T, 96))
+
+
+def test_full_flux_mlp_w2a4_chain():
+    up, down = W["flux_mlp_w2a4"].linears
+    rows = _sample_rows(up.T, 64)
+    y_up = run_linear(up, index=0, act_rows=_sample_rows(up.T, 512), gemm_rows=rows)
+    x_down = y_up.cpu().numpy()
+    _, W_down = synth.gen_linear(down, 0, 1, T=1, need_act=False)
+    run_linear(down, index=1, x=x_down, W_=W_down, x_dtype="f32", act_rows=_sample_rows(down.T, 512),
+               gemm_rows=rows)
+
+
+def test_full_wan_ffn_w4a4():
+    lin = W["wan_ffn_w4a4"].linears[0]
+    run_linear(lin, act_rows=_sample_rows(lin.T, 1024), gemm_rows=_sample_rows(lin.T, 48))
+
+
+def test_full_flux_block_w4a8():
+    for k, lin in enumerate(W["flux_block_w4a8_b2"].linears):
+        run_linear(lin, index=k, act_rows=_sample_rows(lin.T, 256), gemm_rows=_sample_rows(lin.T, 32))

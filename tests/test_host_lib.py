@@ -1,0 +1,110 @@
+"""liboq on the host: it loads, exports every symbol of include/oq.h, its
+host calls agree with the oracle, and invalid arguments are rejected before
+anything is launched (no device compute here)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from free_bit_quantization_amd import oq
+from oracle import codebook, rpbh
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_exports_every_declared_symbol():
+    hdr = open(os.path.join(ROOT, "include", "oq.h")).read()
+    declared = set(re.findall(r"^\s*(?:const char\*|oq_status)\s+(oq_\w+)\s*\(", hdr, re.M))
+    assert declared == set(oq.EXPORTS)
+    L = oq.lib()
+    for name in declared:
+        assert hasattr(L, name)
+    assert oq.oq_version().startswith("liboq")
+
+
+@pytest.mark.parametrize("d,h,seed", [(8, 2, 0), (256, 64, 0), (3072, 256, 0), (5120, 256, 0), (12288, 256, 0), (96, 32, 77)])
+def test_rpbh_bit_identical_to_oracle(d, h, seed):
+    p, s = oq.oq_build_rpbh(d, h, seed)
+    po, so = rpbh.build_rpbh(d, h, seed)
+    np.testing.assert_array_equal(p, po)
+    np.testing.assert_array_equal(s, so)
+
+
+@pytest.mark.parametrize("d,bits", [(3, 2), (256, 1), (256, 4), (3072, 2), (3072, 4), (3072, 8), (5120, 4),
+                                    (12288, 2), (12288, 4), (12288, 8)])
+def test_lloyd_max_agrees_with_oracle(d, bits):
+    c, th, mse = oq.oq_lloyd_max(d, bits)
+    co, tho, mseo, _ = codebook.lloyd_max_fd(d, bits)
+    assert np.max(np.abs(c - co)) <= 1e-9 * np.max(np.abs(co))
+    np.testing.assert_array_equal(th, 0.5 * (c[:-1] + c[1:]))
+    assert abs(mse - mseo) <= 1e-8 * mseo
+    # the library's codebook satisfies the oracle's fixed-point conditions
+    m, _ = codebook.conditional_means(c, codebook.SphereMarginal(d))
+    assert np.max(np.abs(c - m)) <= 1e-10 * np.max(np.abs(c))
+
+
+def test_host_argument_errors():
+    L = oq.lib()
+    perm = np.zeros(8, np.int32)
+    sign = np.zeros(8, np.int8)
+    assert L.oq_build_rpbh(8, 3, 0, perm.ctypes.data, sign.ctypes.data) == oq.OQ_EINVAL
+    assert L.oq_build_rpbh(8, 16, 0, perm.ctypes.data, sign.ctypes.data) == oq.OQ_EINVAL
+    assert L.oq_build_rpbh(8, 2, 0, None, sign.ctypes.data) == oq.OQ_EINVAL
+    assert b"NULL" in L.oq_last_error()
+    c = np.zeros(16)
+    t = np.zeros(15)
+    assert L.oq_lloyd_max(2, 4, c.ctypes.data, t.ctypes.data, None) == oq.OQ_EINVAL
+    assert L.oq_lloyd_max(256, 9, c.ctypes.data, t.ctypes.data, None) == oq.OQ_EINVAL
+    assert L.oq_lloyd_max(256, 4, c.ctypes.data, t.ctypes.data, None) == oq.OQ_OK
+    assert L.oq_last_error() == b""
+
+
+def _fake(n=1 << 20):
+    # never dereferenced: validation fails before any launch
+    return ctypes.c_void_p(n)
+
+
+def test_device_calls_reject_bad_arguments_without_launching():
+    L = oq.lib()
+    _, th, _ = oq.oq_lloyd_max(256, 4)
+    thp = th.ctypes.data
+    bad_th = th.copy()
+    bad_th[3] = bad_th[2]
+    f = _fake()
+    # rotate-quantize
+    args = dict(x=f, dt=oq.OQ_BF16, T=4, d=256, h=64, perm=f, sign=f, th=thp, bits=4, idx=f, s=f, xr=None, st=None)
+
+    def rq(**kw):
+        a = dict(args, **kw)
+        return L.oq_rotate_quantize_act(a["x"], a["dt"], a["T"], a["d"], a["h"], a["perm"], a["sign"], a["th"],
+                                        a["bits"], a["idx"], a["s"], a["xr"], a["st"])
+    assert rq(h=48) == oq.OQ_EINVAL
+    assert rq(h=512) == oq.OQ_EINVAL            # h does not divide d
+    assert rq(d=250) == oq.OQ_EINVAL
+    assert rq(bits=3) == oq.OQ_EINVAL
+    assert rq(T=-1) == oq.OQ_EINVAL
+    assert rq(dt=7) == oq.OQ_EINVAL
+    assert rq(x=None) == oq.OQ_EINVAL
+    assert rq(th=bad_th.ctypes.data) == oq.OQ_EINVAL
+    assert rq(th=None) == oq.OQ_EINVAL
+    assert rq(d=768, h=256) == oq.OQ_EUNSUPPORTED   # d/16 = 48: no kernel plan
+    assert rq(T=0) == oq.OQ_OK                       # valid no-op
+    # weights
+    assert L.oq_quantize_weights(f, oq.OQ_F32, 4, 256, 64, f, f, thp, 3, f, f, None) == oq.OQ_EINVAL
+    assert L.oq_quantize_weights(f, oq.OQ_F32, -1, 256, 64, f, f, thp, 4, f, f, None) == oq.OQ_EINVAL
+    assert L.oq_quantize_weights(None, oq.OQ_F32, 4, 256, 64, f, f, thp, 4, f, f, None) == oq.OQ_EINVAL
+    assert L.oq_quantize_weights(f, oq.OQ_F32, 0, 256, 64, f, f, thp, 4, f, f, None) == oq.OQ_OK
+    # GEMM
+    c, _, _ = oq.oq_lloyd_max(256, 4)
+    c2, _, _ = oq.oq_lloyd_max(256, 2)
+    cp, c2p = c.ctypes.data, c2.ctypes.data
+    assert L.oq_qlinear(f, f, 4, f, f, 8, 256, cp, 4, cp, 3, None, 0, f, None) == oq.OQ_EINVAL
+    assert L.oq_qlinear(f, f, 4, f, f, 8, 256, cp, 4, cp, 4, None, 5, f, None) == oq.OQ_EINVAL
+    assert L.oq_qlinear(f, f, 4, f, f, 8, 256, None, 4, cp, 4, None, 0, f, None) == oq.OQ_EINVAL
+    assert L.oq_qlinear(None, f, 4, f, f, 8, 256, cp, 4, cp, 4, None, 0, f, None) == oq.OQ_EINVAL
+    assert L.oq_qlinear(f, f, 4, f, f, 8, 96, cp, 4, cp, 4, None, 0, f, None) == oq.OQ_EUNSUPPORTED
+    assert L.oq_qlinear(f, f, 4, f, f, 8, 256, c2p, 2, cp, 4, None, 0, f, None) == oq.OQ_EUNSUPPORTED  # A2
+    assert L.oq_qlinear(f, f, 0, f, f, 8, 256, cp, 4, c2p, 2, None, 0, f, None) == oq.OQ_OK
