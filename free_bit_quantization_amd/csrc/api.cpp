@@ -175,7 +175,8 @@ oq_status oq_qlinear(const uint8_t* x_idx, const float* s, int64_t T, const uint
   for (int i = 0; i < Lw; ++i)
     if (!std::isfinite(centroids_w[i])) return fail(OQ_EINVAL, "centroids_w[%d] not finite", i);
   if (T > 0 && d_out > 0 && (!x_idx || !s || !w_idx || !w_norm || !y)) return fail(OQ_EINVAL, "NULL device pointer");
-  if (d_in % 64 != 0) return fail(OQ_EUNSUPPORTED, "d_in must be a multiple of 64 (got %d)", d_in);
+  const int kstage = bits_a == 8 ? 64 : 128;  // K indices per pipeline stage of the GEMM
+  if (d_in % kstage != 0) return fail(OQ_EUNSUPPORTED, "d_in must be a multiple of %d for A%d (got %d)", kstage, bits_a, d_in);
   if (!((bits_a == 4 || bits_a == 8) && (bits_w == 2 || bits_w == 4)))
     return fail(OQ_EUNSUPPORTED, "no GEMM kernel for W%dA%d", bits_w, bits_a);
   const double sk = std::sqrt((double)d_in);

@@ -134,46 +134,60 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
   const float inv_sqrt_h = (float)(1.0 / sqrt((double)H));
   const float og = (float)(-a.g_lo * a.g_invw);
   const int64_t ngroups = (a.T + TPW - 1) / TPW;
+
+  // raw 16 coordinates of this lane's slot, prefetched one token ahead
+  constexpr int NV = BF16 ? 2 : 4;
+  u32x4 raw[NV];
+  auto fetch = [&](int64_t grp) {
+    int64_t tk = grp * TPW + tl;
+    tk = tk < a.T ? tk : a.T - 1;
+    const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const unsigned char*>(a.x) +
+                                                      ((size_t)tk * d + 16 * sl) * ES);
+#pragma unroll
+    for (int k = 0; k < NV; ++k) raw[k] = src[k];
+  };
+  if ((int64_t)blockIdx.x < ngroups) fetch(blockIdx.x);
+
   int par = 0;
   for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x, par ^= 1) {
     const int64_t tok = g * TPW + tl;
     const bool valid = tok < a.T;
-    const int64_t tokc = valid ? tok : a.T - 1;
     const uint32_t paroff = par * (uint32_t)Ly.row_stride;
 
-    // ---- 1. load 16 coordinates [16 sl, 16 sl + 16), sum of squares ----------
+    // ---- 1. stage the prefetched coordinates [16 sl, 16 sl + 16), sum of squares
     float q0 = 0.f, q1 = 0.f, q2 = 0.f, q3 = 0.f;
     {
-      unsigned char* rowdst = smem + Ly.row + paroff + ((size_t)tl * d + 16 * sl) * ES;
-      if (BF16) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(a.x) + tokc * d + 16 * sl);
-        const u32x4 v0 = src[0];
-        const u32x4 v1 = src[1];
-        reinterpret_cast<u32x4*>(rowdst)[0] = v0;
-        reinterpret_cast<u32x4*>(rowdst)[1] = v1;
-        const uint32_t w[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      u32x4* rowdst = reinterpret_cast<u32x4*>(smem + Ly.row + paroff + ((size_t)tl * d + 16 * sl) * ES);
 #pragma unroll
-        for (int k = 0; k < 8; k += 2) {
-          const float e0 = __uint_as_float(w[k] << 16), e1 = __uint_as_float(w[k] & 0xFFFF0000u);
-          const float e2 = __uint_as_float(w[k + 1] << 16), e3 = __uint_as_float(w[k + 1] & 0xFFFF0000u);
+      for (int k = 0; k < NV; ++k) rowdst[k] = raw[k];
+      if (BF16) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+#pragma unroll
+          for (int q = 0; q < 4; q += 2) {
+            const uint32_t w0 = raw[k][q], w1 = raw[k][q + 1];
+            const float e0 = __uint_as_float(w0 << 16), e1 = __uint_as_float(w0 & 0xFFFF0000u);
+            const float e2 = __uint_as_float(w1 << 16), e3 = __uint_as_float(w1 & 0xFFFF0000u);
+            q0 = fmaf(e0, e0, q0);
+            q1 = fmaf(e1, e1, q1);
+            q2 = fmaf(e2, e2, q2);
+            q3 = fmaf(e3, e3, q3);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float e0 = __uint_as_float(raw[k][0]), e1 = __uint_as_float(raw[k][1]);
+          const float e2 = __uint_as_float(raw[k][2]), e3 = __uint_as_float(raw[k][3]);
           q0 = fmaf(e0, e0, q0);
           q1 = fmaf(e1, e1, q1);
           q2 = fmaf(e2, e2, q2);
           q3 = fmaf(e3, e3, q3);
         }
-      } else {
-        const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(a.x) + tokc * d + 16 * sl);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const f32x4 v = src[k];
-          reinterpret_cast<f32x4*>(rowdst)[k] = v;
-          q0 = fmaf(v.x, v.x, q0);
-          q1 = fmaf(v.y, v.y, q1);
-          q2 = fmaf(v.z, v.z, q2);
-          q3 = fmaf(v.w, v.w, q3);
-        }
       }
     }
+    // the next token's row is in flight while this one is processed
+    if (g + gridDim.x < ngroups) fetch(g + gridDim.x);
     double ss = (double)((q0 + q1) + (q2 + q3));
     if (NS >= 64) {
 #pragma unroll
@@ -223,15 +237,18 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
       }
     }
     if (TWO_PASS) {
+      // element i of the block lives at row i/16 (its pass-2 lane), column
+      // chunk (i/4 % 4) ^ (row/4 % 4): the 16 lanes of a block then hit 64
+      // distinct banks with their 16-byte reads
       float* tb = reinterpret_cast<float*>(smem + Ly.trans) + ((size_t)tl * (d / H) + sl / BL) * (H + kPad);
       const int t = sl % BL;
+      auto swz = [](int i) { return (i & ~15) | ((((i >> 2) & 3) ^ ((i >> 6) & 3)) << 2) | (i & 3); };
 #pragma unroll
-      for (int r = 0; r < 16; ++r) tb[r * BL + t] = y[r];
+      for (int r = 0; r < 16; ++r) tb[swz(r * BL + t)] = y[r];
       wave_sync_lds();
-      const f32x4* rd = reinterpret_cast<const f32x4*>(tb + t * 16);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const f32x4 v = rd[k];
+        const f32x4 v = *reinterpret_cast<const f32x4*>(tb + swz(t * 16 + 4 * k));
         y[4 * k] = v.x; y[4 * k + 1] = v.y; y[4 * k + 2] = v.z; y[4 * k + 3] = v.w;
       }
 #pragma unroll
@@ -252,38 +269,50 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
     // ---- 4./5. threshold search and guard ----------------------------------------
     uint64_t pk0 = 0, pk1 = 0;  // packed indices (pk1 only for 8-bit)
     uint32_t flags = 0;
+    int idx[16];
+    if (G > 0) {
+      int ci[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float v = y[r];
-      const float radb = kGam * l1[TWO_PASS ? 0 : r / (16 / BPL)] * c;
-      int idx;
-      if (G > 0) {
-        const int ci = (int)__builtin_amdgcn_fmed3f(fmaf(v, cg, og), 0.0f, (float)(G - 1));
-        const int2 e = lut[ci];
-        const float th = __int_as_float(e.x);
-        const float dd = fmaf(v, c, -th);
-        idx = e.y + (dd > 0.f ? 1 : 0);
-        if (fabsf(dd) < fmaf(fabsf(th), kRel, radb)) flags |= 1u << r;
-      } else {
+      for (int r = 0; r < 16; ++r) ci[r] = (int)__builtin_amdgcn_fmed3f(fmaf(y[r], cg, og), 0.0f, (float)(G - 1));
+      int2 e[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) e[r] = lut[ci[r]];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float radb = kGam * l1[TWO_PASS ? 0 : r / (16 / BPL)] * c;
+        const float th = __int_as_float(e[r].x);
+        const float dd = fmaf(y[r], c, -th);
+        idx[r] = e[r].y + (dd > 0.f ? 1 : 0);
+        flags |= (fabsf(dd) < fmaf(fabsf(th), kRel, radb) ? 1u : 0u) << r;
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float v = y[r];
+        const float radb = kGam * l1[TWO_PASS ? 0 : r / (16 / BPL)] * c;
         int lo = 0;
-#pragma unroll
         for (int step = 128; step >= 1; step >>= 1)
           if (lo + step <= nthr && fmaf(v, c, -thr[lo + step - 1]) > 0.f) lo += step;
-        idx = lo;
+        idx[r] = lo;
+        bool near = false;
         if (lo > 0) {
           const float th = thr[lo - 1];
-          if (fabsf(fmaf(v, c, -th)) < fmaf(fabsf(th), kRel, radb)) flags |= 1u << r;
+          near |= fabsf(fmaf(v, c, -th)) < fmaf(fabsf(th), kRel, radb);
         }
         if (lo < nthr) {
           const float th = thr[lo];
-          if (fabsf(fmaf(v, c, -th)) < fmaf(fabsf(th), kRel, radb)) flags |= 1u << r;
+          near |= fabsf(fmaf(v, c, -th)) < fmaf(fabsf(th), kRel, radb);
         }
+        flags |= (near ? 1u : 0u) << r;
       }
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
       if (BITS == 8) {
-        if (r < 8) pk0 |= (uint64_t)idx << (8 * r);
-        else pk1 |= (uint64_t)idx << (8 * (r - 8));
+        if (r < 8) pk0 |= (uint64_t)idx[r] << (8 * r);
+        else pk1 |= (uint64_t)idx[r] << (8 * (r - 8));
       } else {
-        pk0 |= (uint64_t)idx << (BITS * r);
+        pk0 |= (uint64_t)idx[r] << (BITS * r);
       }
     }
     if (!valid) flags = 0;
@@ -414,12 +443,28 @@ hipError_t allow_lds(K kernel, bool& done) {
   return e;
 }
 
+int device_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      cus = 256;
+  }
+  return cus;
+}
+
 template <int LOG2H, bool BF16, int BITS>
 hipError_t rq_go(const RqArgs& a, const RqPlan& p, hipStream_t st) {
   static bool attr = false;
   hipError_t e = allow_lds(&rq_act_kernel<LOG2H, BF16, BITS>, attr);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((rq_act_kernel<LOG2H, BF16, BITS>), dim3(p.grid), dim3(p.threads), p.lds, st, a, p.ns, p.tpw);
+  // persistent grid: as many workgroups as are resident at once, each looping over tokens
+  int per_cu = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, rq_act_kernel<LOG2H, BF16, BITS>, p.threads, p.lds);
+  if (e != hipSuccess) return e;
+  const int64_t resident = (int64_t)(per_cu > 0 ? per_cu : 1) * device_cus();
+  const int grid = (int)(p.grid < resident ? p.grid : resident);
+  hipLaunchKernelGGL((rq_act_kernel<LOG2H, BF16, BITS>), dim3(grid), dim3(p.threads), p.lds, st, a, p.ns, p.tpw);
   return hipGetLastError();
 }
 
@@ -473,9 +518,7 @@ bool rq_plan(int32_t d, int32_t log2h, bool bf16, int64_t T, int G, RqPlan* p) {
   p->lds = L.total;
   if (p->lds > 160 * 1024) return false;
   const int64_t groups = (T + tpw - 1) / tpw;
-  // up to 8 resident workgroups on each of the 256 CUs; each loops over token groups
-  const int64_t cap = 256 * 8;
-  p->grid = (int)(groups < cap ? (groups > 0 ? groups : 1) : cap);
+  p->grid = (int)(groups < (1 << 30) ? (groups > 0 ? groups : 1) : (1 << 30));  // capped at launch by residency
   return true;
 }
 

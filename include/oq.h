@@ -166,7 +166,8 @@ oq_status oq_rotate_quantize_act(const void* x, oq_dtype x_dtype, int64_t T, int
  *
  * x_idx       : dev [T][d_in * bits_a / 8], from oq_rotate_quantize_act.
  * s           : dev [T] float.
- * T           : tokens >= 0.   d_out >= 0.   d_in: multiple of 64.
+ * T           : tokens >= 0.   d_out >= 0.   d_in: multiple of 128 (bits_a = 4)
+ *               or of 64 (bits_a = 8).
  * w_idx       : dev [d_out][d_in * bits_w / 8], from oq_quantize_weights.
  * w_norm      : dev [d_out] float.
  * centroids_a : host [2^bits_a] double, ascending.  bits_a: 4 or 8.
