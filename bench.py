@@ -28,6 +28,25 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, TFLOP/s
 
+# HBM bytes per launch from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of this
+# bench (FETCH_SIZE x 2, WRITE_SIZE x 1: the copy-kernel calibration), valid only
+# for the kernel source they were taken on (sha256 prefix); otherwise null.
+MEASURED_TRAFFIC = {
+    "free_bit_quantization_amd/csrc/qlinear.hip": ("3f48169dda562474", 119.6e6, 169.9e6),
+    "free_bit_quantization_amd/csrc/rotate_quantize.hip": ("4854a2d20dbcd21d", 28.7e6, 7.2e6),
+}
+
+
+def traffic_of(src: str):
+    import hashlib
+    entry = MEASURED_TRAFFIC.get(src)
+    if entry is None:
+        return None
+    digest = hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest()[:16]
+    if digest != entry[0]:
+        return None
+    return entry[1] + entry[2]
+
 
 def cpu_baseline(lin, x, Wm, perm, sign, c_a, th_a, c_w, th_w, target_s: float = 12.0):
     """The fp64 oracle on the host cores, on a bounded sample of tokens of the
@@ -162,10 +181,13 @@ def main():
         "rotate_quant_GBps": round(rq_gbs, 1),
         "rotate_quant_ms": round(t_rq, 5),
         "roofline": {"bound": "mfma", "achieved": round(ql_tflops, 2), "peak": FP16_MFMA_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(ql_tflops / FP16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(ql_tflops / FP16_MFMA_PEAK_TFLOPS, 4),
+                     "traffic": traffic_of("free_bit_quantization_amd/csrc/qlinear.hip"), "traffic_unit": "bytes",
                      "kernel": "oq_qlinear (ql_kernel<4,4>)", "algorithmic": f"2*T*K*N = {flops:.4g} flop"},
         "roofline_rotate_quant": {"bound": "hbm", "achieved": round(rq_gbs, 1), "peak": HBM_PEAK_GBS,
-                                  "unit": "GB/s", "frac": round(rq_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                                  "unit": "GB/s", "frac": round(rq_gbs / HBM_PEAK_GBS, 4),
+                                  "traffic": traffic_of("free_bit_quantization_amd/csrc/rotate_quantize.hip"),
+                                  "traffic_unit": "bytes",
                                   "kernel": "oq_rotate_quantize_act (rq_act_kernel<8,bf16,4>)",
                                   "algorithmic": f"T*(K*{es} + K*{lin.bits_a}/8 + 4) = {rq_bytes} B"},
         "wall_s_timed": round(t_wall, 4),

@@ -46,6 +46,43 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+
+// ---- cross-lane sums on DPP (VALU latency instead of an LDS round trip) -----
+// Stages pair lane i with i^1, i^2 (quad_perm), 7-i within 8 (row_half_mirror)
+// and 15-i within 16 (row_mirror); each stage adds symmetric pairs, so every
+// lane of a group ends with the bitwise-same total.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+// all-reduce over aligned groups of G lanes, G a power of two <= 16
+template <int G, typename F>
+__device__ __forceinline__ F group_sum(F v) {
+  if constexpr (G >= 2) { if constexpr (sizeof(F) == 4) v += dpp_f<0xB1>(v); else v += dpp_d<0xB1>(v); }
+  if constexpr (G >= 4) { if constexpr (sizeof(F) == 4) v += dpp_f<0x4E>(v); else v += dpp_d<0x4E>(v); }
+  if constexpr (G >= 8) { if constexpr (sizeof(F) == 4) v += dpp_f<0x141>(v); else v += dpp_d<0x141>(v); }
+  if constexpr (G >= 16) { if constexpr (sizeof(F) == 4) v += dpp_f<0x140>(v); else v += dpp_d<0x140>(v); }
+  return v;
+}
+__device__ __forceinline__ double readlane_d(double v, int lane) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+// sum over the whole wavefront, same value in every lane, fixed order
+__device__ __forceinline__ double wave_sum_d(double v) {
+  v = group_sum<16>(v);
+  return (readlane_d(v, 0) + readlane_d(v, 16)) + (readlane_d(v, 32) + readlane_d(v, 48));
+}
+
 __host__ __device__ inline size_t align16(size_t v) { return (v + 15) & ~size_t(15); }
 
 struct RqLayout {
@@ -190,11 +227,15 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
     if (g + gridDim.x < ngroups) fetch(g + gridDim.x);
     double ss = (double)((q0 + q1) + (q2 + q3));
     if (NS >= 64) {
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+      ss = wave_sum_d(ss);
       if (lane == 0) red[par * 16 + wave] = ss;
     } else {
-      for (int o = NS >> 1; o >= 1; o >>= 1) ss += __shfl_xor(ss, o);
+      // groups of NS lanes (a power of two below 64)
+      if (NS >= 16) ss = group_sum<16>(ss);
+      else if (NS == 8) ss = group_sum<8>(ss);
+      else if (NS == 4) ss = group_sum<4>(ss);
+      else if (NS == 2) ss = group_sum<2>(ss);
+      if (NS == 32) ss += __shfl_xor(ss, 16);
     }
     __syncthreads();
     if (NS >= 64) {
@@ -262,28 +303,39 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
           }
         }
       }
-#pragma unroll
-      for (int o = 1; o < BL; o <<= 1) l1[0] += __shfl_xor(l1[0], o);
+      l1[0] = group_sum<BL>(l1[0]);
     }
 
     // ---- 4./5. threshold search and guard ----------------------------------------
     uint64_t pk0 = 0, pk1 = 0;  // packed indices (pk1 only for 8-bit)
     uint32_t flags = 0;
-    int idx[16];
+    auto put = [&](int r, int idx) {
+      if (BITS == 8) {
+        if (r < 8) pk0 |= (uint64_t)idx << (8 * r);
+        else pk1 |= (uint64_t)idx << (8 * (r - 8));
+      } else {
+        pk0 |= (uint64_t)idx << (BITS * r);
+      }
+    };
     if (G > 0) {
-      int ci[16];
+      // two halves of 8: all LUT reads of a half are in flight together
 #pragma unroll
-      for (int r = 0; r < 16; ++r) ci[r] = (int)__builtin_amdgcn_fmed3f(fmaf(y[r], cg, og), 0.0f, (float)(G - 1));
-      int2 e[16];
+      for (int hf = 0; hf < 2; ++hf) {
+        int2 e[8];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) e[r] = lut[ci[r]];
+        for (int q = 0; q < 8; ++q) {
+          const int ci = (int)__builtin_amdgcn_fmed3f(fmaf(y[8 * hf + q], cg, og), 0.0f, (float)(G - 1));
+          e[q] = lut[ci];
+        }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float radb = kGam * l1[TWO_PASS ? 0 : r / (16 / BPL)] * c;
-        const float th = __int_as_float(e[r].x);
-        const float dd = fmaf(y[r], c, -th);
-        idx[r] = e[r].y + (dd > 0.f ? 1 : 0);
-        flags |= (fabsf(dd) < fmaf(fabsf(th), kRel, radb) ? 1u : 0u) << r;
+        for (int q = 0; q < 8; ++q) {
+          const int r = 8 * hf + q;
+          const float radb = kGam * l1[TWO_PASS ? 0 : r / (16 / BPL)] * c;
+          const float th = __int_as_float(e[q].x);
+          const float dd = fmaf(y[r], c, -th);
+          put(r, e[q].y + (dd > 0.f ? 1 : 0));
+          flags |= (fabsf(dd) < fmaf(fabsf(th), kRel, radb) ? 1u : 0u) << r;
+        }
       }
     } else {
 #pragma unroll
@@ -293,7 +345,6 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
         int lo = 0;
         for (int step = 128; step >= 1; step >>= 1)
           if (lo + step <= nthr && fmaf(v, c, -thr[lo + step - 1]) > 0.f) lo += step;
-        idx[r] = lo;
         bool near = false;
         if (lo > 0) {
           const float th = thr[lo - 1];
@@ -303,16 +354,8 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
           const float th = thr[lo];
           near |= fabsf(fmaf(v, c, -th)) < fmaf(fabsf(th), kRel, radb);
         }
+        put(r, lo);
         flags |= (near ? 1u : 0u) << r;
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      if (BITS == 8) {
-        if (r < 8) pk0 |= (uint64_t)idx[r] << (8 * r);
-        else pk1 |= (uint64_t)idx[r] << (8 * (r - 8));
-      } else {
-        pk0 |= (uint64_t)idx[r] << (BITS * r);
       }
     }
     if (!valid) flags = 0;
@@ -343,8 +386,7 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
           }
         }
       }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o);
+      part = wave_sum_d(part);
       if (lane == L) {
         const double u = part / (sqrt((double)H) * (s64 + OQ_EPS));
         const uint64_t nidx = (uint64_t)count_below_f64(thr, nthr, u);
