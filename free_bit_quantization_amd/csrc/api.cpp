@@ -122,6 +122,8 @@ oq_status oq_rotate_quantize_act(const void* x, oq_dtype x_dtype, int64_t T, int
   oq_status st = check_thresholds(thresholds, nthr, true);
   if (st != OQ_OK) return st;
   if (T > 0 && (!x || !perm || !sign || !x_idx || !s)) return fail(OQ_EINVAL, "NULL device pointer");
+  if (((reinterpret_cast<uintptr_t>(x) | reinterpret_cast<uintptr_t>(x_idx) | reinterpret_cast<uintptr_t>(x_rot)) & 15) != 0)
+    return fail(OQ_EINVAL, "x, x_idx and x_rot must be 16-byte aligned");
   if (m > 8) return fail(OQ_EUNSUPPORTED, "h > 256 has no kernel");
 
   // Threshold-search grid: cells of width w over [theta_0, theta_{L-2}], each
@@ -175,6 +177,9 @@ oq_status oq_qlinear(const uint8_t* x_idx, const float* s, int64_t T, const uint
   for (int i = 0; i < Lw; ++i)
     if (!std::isfinite(centroids_w[i])) return fail(OQ_EINVAL, "centroids_w[%d] not finite", i);
   if (T > 0 && d_out > 0 && (!x_idx || !s || !w_idx || !w_norm || !y)) return fail(OQ_EINVAL, "NULL device pointer");
+  auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; };
+  if (misaligned(x_idx) || misaligned(w_idx) || misaligned(w_norm) || misaligned(y) || misaligned(bias))
+    return fail(OQ_EINVAL, "x_idx, w_idx, w_norm, bias and y must be 16-byte aligned");
   const int kstage = bits_a == 8 ? 64 : 128;  // K indices per pipeline stage of the GEMM
   if (d_in % kstage != 0) return fail(OQ_EUNSUPPORTED, "d_in must be a multiple of %d for A%d (got %d)", kstage, bits_a, d_in);
   if (!((bits_a == 4 || bits_a == 8) && (bits_w == 2 || bits_w == 4)))

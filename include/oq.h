@@ -145,6 +145,7 @@ oq_status oq_quantize_weights(const void* W, oq_dtype w_dtype, int32_t d_out, in
  * x_idx      : dev [T][d * bits_a / 8] bytes, written.
  * s          : dev [T] float, written (the norm, without eps).
  * x_rot      : dev [T][d] float or NULL: the fp32 rotated rows (checking only).
+ * x, x_idx and x_rot must be 16-byte aligned (OQ_EINVAL otherwise).
  * Errors     : OQ_EINVAL, OQ_EUNSUPPORTED, OQ_EDEVICE.
  */
 oq_status oq_rotate_quantize_act(const void* x, oq_dtype x_dtype, int64_t T, int32_t d, int32_t h,
@@ -175,6 +176,7 @@ oq_status oq_rotate_quantize_act(const void* x, oq_dtype x_dtype, int64_t T, int
  * bias        : dev [d_out] float or NULL.
  * epilogue    : OQ_EPI_NONE or OQ_EPI_GELU_ERF.
  * y           : dev [T][d_out] float, written.
+ * x_idx, w_idx, w_norm, bias and y must be 16-byte aligned (OQ_EINVAL otherwise).
  * Errors      : OQ_EINVAL, OQ_EUNSUPPORTED, OQ_EDEVICE.
  */
 oq_status oq_qlinear(const uint8_t* x_idx, const float* s, int64_t T,

@@ -91,6 +91,8 @@ def test_device_calls_reject_bad_arguments_without_launching():
     assert rq(th=bad_th.ctypes.data) == oq.OQ_EINVAL
     assert rq(th=None) == oq.OQ_EINVAL
     assert rq(d=768, h=256) == oq.OQ_EUNSUPPORTED   # d/16 = 48: no kernel plan
+    assert rq(x=_fake((1 << 20) + 4)) == oq.OQ_EINVAL   # 16-byte vector loads need alignment
+    assert rq(idx=_fake((1 << 20) + 8)) == oq.OQ_EINVAL
     assert rq(T=0) == oq.OQ_OK                       # valid no-op
     # weights
     assert L.oq_quantize_weights(f, oq.OQ_F32, 4, 256, 64, f, f, thp, 3, f, f, None) == oq.OQ_EINVAL
@@ -108,3 +110,7 @@ def test_device_calls_reject_bad_arguments_without_launching():
     assert L.oq_qlinear(f, f, 4, f, f, 8, 96, cp, 4, cp, 4, None, 0, f, None) == oq.OQ_EUNSUPPORTED
     assert L.oq_qlinear(f, f, 4, f, f, 8, 256, c2p, 2, cp, 4, None, 0, f, None) == oq.OQ_EUNSUPPORTED  # A2
     assert L.oq_qlinear(f, f, 0, f, f, 8, 256, cp, 4, c2p, 2, None, 0, f, None) == oq.OQ_OK
+    g = _fake((1 << 20) + 4)
+    assert L.oq_qlinear(g, f, 4, f, f, 8, 256, cp, 4, cp, 4, None, 0, f, None) == oq.OQ_EINVAL
+    assert L.oq_qlinear(f, f, 4, f, f, 8, 256, cp, 4, cp, 4, g, 0, f, None) == oq.OQ_EINVAL   # bias
+    assert L.oq_qlinear(f, f, 4, f, f, 8, 256, cp, 4, cp, 4, None, 0, g, None) == oq.OQ_EINVAL   # y
