@@ -43,6 +43,8 @@ struct RqPlan {
   int threads;   // workgroup size
   int grid;      // workgroups
   size_t lds;    // dynamic LDS bytes
+  int wave_j;    // > 0: one wavefront per token, wave_j slots of 16 coordinates per lane
+  int wpb;       // wavefronts per workgroup of that kernel
 };
 
 // Returns false if (d, h) has no kernel.

@@ -26,8 +26,14 @@
 //      recomputed in fp64 by the wavefront (rare) before its index is set;
 //   6. LSB-first packing of 2 / 4 / 8-bit indices, one 4 / 8 / 16-byte store.
 //
+// Rows of d = 1024 J coordinates (J <= 3) with h = 64 or 256 take a second
+// mapping of the same steps, rq_wave_kernel: a wavefront owns whole tokens
+// (48 coordinates per lane at J = 3), so no workgroup barrier is needed after
+// the set-up and every wavefront keeps its own token row in flight.
+//
 // Weight kernel (offline): one workgroup per row, fp64 throughout.
 #include <cmath>
+#include <type_traits>
 
 #include "oq_internal.h"
 
@@ -419,6 +425,328 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
   }
 }
 
+// ---- activations, one wavefront per token (d = 1024 J, J <= 3, h = 64 or 256) ----
+// The same computation as rq_act_kernel with a different mapping: a
+// wavefront owns whole tokens, lane l stages the 16-coordinate chunks
+// l, l + 64, ... of the row (coalesced), the norm is a wavefront sum, and
+// slot j of lane l holds the pass-1 elements of coordinates [1024 j,
+// 1024 j + 1024) exactly as slot 64 j + l of rq_act_kernel.  No barrier is
+// needed after the set-up, so each wavefront runs its tokens independently
+// and a CU keeps one token row in flight per wavefront.  Sign flips are
+// applied while staging (sign'_perm(i) = sign_i), and only the grid search is
+// built here (the host uses rq_act_kernel when the grid is empty).
+struct RqwLayout {
+  size_t thr, lut, mtab, atab, wave0, row_bytes, wave_bytes, total;
+};
+
+__host__ __device__ inline RqwLayout rqw_layout(int d, int log2h, int es, int G, int wpb) {
+  RqwLayout L;
+  const int h = 1 << log2h;
+  L.thr = 0;
+  L.lut = 256 * 4;
+  L.mtab = L.lut + align16(8 * (size_t)(G > 0 ? G : 1));
+  const size_t mwords = es == 2 ? (size_t)d / 2 : (size_t)d;   // sign masks of the source words
+  L.atab = L.mtab + align16(4 * mwords);                          // gather offsets, 4 d bytes
+  L.wave0 = L.atab + align16(4 * (size_t)d);
+  L.row_bytes = align16((size_t)d * es);
+  L.wave_bytes = L.row_bytes + align16((size_t)(1024 / h) * (h + kPad) * 4);
+  L.total = L.wave0 + (size_t)wpb * L.wave_bytes;
+  const size_t setup = L.wave0 + align16((size_t)d);   // sign' bytes over the wave buffers
+  if (setup > L.total) L.total = setup;
+  return L;
+}
+
+template <int LOG2H, bool BF16, int BITS, int J>
+__global__ void __launch_bounds__(768) rq_wave_kernel(const RqArgs a, const int WPB) {
+  constexpr int H = 1 << LOG2H;
+  constexpr int ES = BF16 ? 2 : 4;
+  constexpr int BL = H / 16;                       // lanes per Hadamard block (h >= 32: two passes)
+  static_assert(LOG2H >= 5 && LOG2H <= 8, "two-pass block sizes only");
+  constexpr float kGam = 2.0f * (LOG2H + 1) * 5.9604644775390625e-8f;  // 2 (m+1) 2^-24
+  constexpr float kRel = 16.0f * 5.9604644775390625e-8f;               // 16 ulp of |theta|
+  constexpr int PER = 32 / BITS;                   // indices per packed 32-bit word
+  constexpr int NW = 16 / PER;                     // packed words per slot
+  constexpr int NV = BF16 ? 2 : 4;                 // 16-byte loads per 16-coordinate chunk
+  constexpr int MW = BF16 ? 8 : 16;                // sign-mask words per chunk
+  constexpr int d = 1024 * J;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int G = a.G;
+  const int nthr = a.nthr;
+  const int64_t T = a.T;
+  const int64_t nwaves = (int64_t)gridDim.x * WPB;
+  // tokens of wavefront w of workgroup b: b + grid (w + WPB k), so that every
+  // workgroup (CU) gets the same share of the tokens
+  const int64_t gw = (int64_t)blockIdx.x + (int64_t)gridDim.x * wave;
+
+  extern __shared__ __align__(16) unsigned char smem[];
+  const RqwLayout Ly = rqw_layout(d, LOG2H, ES, G, WPB);
+  float* thr = reinterpret_cast<float*>(smem + Ly.thr);
+  int2* lut = reinterpret_cast<int2*>(smem + Ly.lut);
+  uint32_t* mtab = reinterpret_cast<uint32_t*>(smem + Ly.mtab);
+  unsigned char* wrow = smem + Ly.wave0 + (size_t)wave * Ly.wave_bytes;   // this wavefront's row
+  float* wtr = reinterpret_cast<float*>(wrow + Ly.row_bytes);           // and transpose buffer
+
+  // raw chunks l + 64 i of the first token, requested before the set-up
+  u32x4 raw[J][NV];
+  auto fetch = [&](int64_t tok) {
+    tok = tok < T ? tok : T - 1;
+#pragma unroll
+    for (int i = 0; i < J; ++i) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(static_cast<const unsigned char*>(a.x) +
+                                                        ((size_t)tok * d + 16 * (lane + 64 * i)) * ES);
+#pragma unroll
+      for (int k = 0; k < NV; ++k) raw[i][k] = src[k];
+    }
+  };
+  if (gw < T) fetch(gw);
+
+  // ---- set-up: thresholds, grid, sign masks, gather addresses ---------------
+  for (int i = tid; i < 256; i += blockDim.x) thr[i] = i < nthr ? a.thr[i] : INFINITY;
+  int8_t* sp = reinterpret_cast<int8_t*>(smem + Ly.wave0);   // sign' scratch over the wave buffers
+  {
+    // d <= 4096 and blockDim >= 256: at most 16 entries per thread
+    int pj[16];
+    int8_t sj[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int i = tid + k * (int)blockDim.x;
+      pj[k] = i < d ? (int)min((unsigned)a.perm[i], (unsigned)(d - 1)) : 0;  // perm is a permutation
+      sj[k] = i < d ? a.sign[i] : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (tid + k * (int)blockDim.x < d) sp[pj[k]] = sj[k];
+  }
+  // pass-1 element r of slot j of lane l has coordinate gin(j, l, r); its row
+  // offset perm(gin) * ES sits at atab[((4 j + r / 4) * 64 + l) * 4 + r % 4], so
+  // a slot's 16 offsets are four conflict-free 16-byte reads per lane
+  auto gin = [&](int j, int l, int r) { return 1024 * j + (l / BL) * H + r * BL + (l % BL); };
+  uint32_t* atab = reinterpret_cast<uint32_t*>(smem + Ly.atab);
+  {
+    int pj[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int e = tid + k * (int)blockDim.x;   // table entry: ((4 j + q) * 64 + l) * 4 + kk
+      const int kk = e & 3, l = (e >> 2) & 63, jq = e >> 8;
+      pj[k] = e < d ? (int)min((unsigned)a.perm[gin(jq >> 2, l, 4 * (jq & 3) + kk)], (unsigned)(d - 1)) : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int e = tid + k * (int)blockDim.x;
+      if (e < d) atab[e] = (uint32_t)pj[k] * ES;
+    }
+  }
+  __syncthreads();
+  if (G > 0) {
+    const double w = 1.0 / a.g_invw;
+    for (int c = tid; c < G; c += blockDim.x) {
+      const double ulo = c == 0 ? -INFINITY : a.g_lo + (c - 0.02) * w - a.g_rmax;
+      const double uhi = c == G - 1 ? INFINITY : a.g_lo + (c + 1.02) * w + a.g_rmax;
+      const int base = count_below_f64(thr, nthr, ulo);
+      const float th = (base < nthr && (double)thr[base] <= uhi) ? thr[base] : INFINITY;
+      lut[c] = make_int2(__float_as_int(th), base);
+    }
+  }
+  for (int i = tid; i < d / (16 / MW); i += blockDim.x) {
+    uint32_t m;
+    if (BF16) m = (sp[2 * i] < 0 ? 0x8000u : 0u) | (sp[2 * i + 1] < 0 ? 0x80000000u : 0u);
+    else m = sp[i] < 0 ? 0x80000000u : 0u;
+    mtab[i] = m;
+  }
+  __syncthreads();  // tables complete, sign scratch consumed
+
+  const float thmax = nthr > 0 ? fmaxf(fabsf(thr[0]), fabsf(thr[nthr - 1])) : 0.f;
+  const float inv_sqrt_h = (float)(1.0 / sqrt((double)H));
+  const float kSqrtH = (float)sqrt((double)H);
+  const float og = (float)(-a.g_lo * a.g_invw);
+  const float ginvw = (float)a.g_invw;
+
+  for (int64_t tok = gw; tok < T; tok += nwaves) {
+    // ---- 1. signed staging of the row, sum of squares --------------------------
+    float q0 = 0.f, q1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < J; ++i) {
+      const int k = lane + 64 * i;   // chunk: coordinates [16 k, 16 k + 16)
+      const u32x4* mk = reinterpret_cast<const u32x4*>(mtab + k * MW);
+      u32x4* dst = reinterpret_cast<u32x4*>(wrow + (size_t)16 * k * ES);
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const u32x4 m = mk[v];
+        u32x4 w = raw[i][v];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (BF16) {
+            const float e0 = __uint_as_float(w[q] << 16), e1 = __uint_as_float(w[q] & 0xFFFF0000u);
+            q0 = fmaf(e0, e0, q0);
+            q1 = fmaf(e1, e1, q1);
+          } else {
+            const float e = __uint_as_float(w[q]);
+            if (q & 1) q1 = fmaf(e, e, q1);
+            else q0 = fmaf(e, e, q0);
+          }
+        }
+        dst[v] = w ^ m;
+      }
+    }
+    // registers free again: the next token's row is in flight from here on
+    if (tok + nwaves < T) fetch(tok + nwaves);
+    const double ss = wave_sum_d((double)(q0 + q1));
+    // fp32 scale for the fast path (a few ulp, inside the guard's 16 ulp of |theta|)
+    const float s32 = sqrtf((float)ss);
+    const float c = 1.0f / (kSqrtH * (s32 + (float)OQ_EPS));
+    const float cg = c * ginvw;
+    wave_sync_lds();  // the staged row is visible to every lane
+
+    const uint32_t rowbase = (uint32_t)(Ly.wave0 + (size_t)wave * Ly.wave_bytes);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      // ---- 2. gather ---------------------------------------------------------------
+      uint32_t addr[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x4 o = reinterpret_cast<const u32x4*>(atab)[(4 * j + q) * 64 + lane];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) addr[4 * q + k] = rowbase + o[k];
+      }
+      float y[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (BF16) y[r] = __uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t*>(smem + addr[r])) << 16);
+        else y[r] = *reinterpret_cast<const float*>(smem + addr[r]);
+      }
+      float l1 = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) l1 += fabsf(y[r]);
+
+      // ---- 3. block FWHT: 16 points in registers, transpose, log2(h) - 4 stages --
+#pragma unroll
+      for (int st = 1; st < 16; st <<= 1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if (!(r & st)) {
+            const float p = y[r], q = y[r + st];
+            y[r] = p + q;
+            y[r + st] = p - q;
+          }
+        }
+      }
+      {
+        float* tb = wtr + (size_t)(lane / BL) * (H + kPad);
+        const int t = lane % BL;
+        auto swz = [](int i) { return (i & ~15) | ((((i >> 2) & 3) ^ ((i >> 6) & 3)) << 2) | (i & 3); };
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tb[swz(r * BL + t)] = y[r];
+        wave_sync_lds();
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(tb + swz(t * 16 + 4 * k));
+          y[4 * k] = v.x; y[4 * k + 1] = v.y; y[4 * k + 2] = v.z; y[4 * k + 3] = v.w;
+        }
+        wave_sync_lds();  // reads done before the next slot overwrites the buffer
+      }
+#pragma unroll
+      for (int st = 1; st < BL; st <<= 1) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if (!(r & st)) {
+            const float p = y[r], q = y[r + st];
+            y[r] = p + q;
+            y[r + st] = p - q;
+          }
+        }
+      }
+      l1 = group_sum<BL>(l1);
+
+      // ---- 4./5. grid search and guard --------------------------------------------
+      const float rad = fmaf(thmax, kRel, kGam * l1 * c);
+      uint32_t pw[NW];
+#pragma unroll
+      for (int k = 0; k < NW; ++k) pw[k] = 0;
+      bool near = false;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        int2 e[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int ci = (int)__builtin_amdgcn_fmed3f(fmaf(y[8 * hf + q], cg, og), 0.0f, (float)(G - 1));
+          e[q] = lut[ci];
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int r = 8 * hf + q;
+          const float dd = fmaf(y[r], c, -__int_as_float(e[q].x));
+          const uint32_t idx = (uint32_t)e[q].y + (dd > 0.f ? 1u : 0u);
+          pw[r / PER] |= idx << (BITS * (r % PER));
+          near |= fabsf(dd) < rad;
+        }
+      }
+
+      // fp64 recheck of guarded coordinates, by the whole wavefront (rare)
+      if (__ballot(near) != 0) {
+        uint32_t flags = 0;
+        if (near) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int ci = (int)__builtin_amdgcn_fmed3f(fmaf(y[r], cg, og), 0.0f, (float)(G - 1));
+            const bool nr = fabsf(fmaf(y[r], c, -__int_as_float(lut[ci].x))) < rad;
+            flags |= (nr ? 1u : 0u) << r;
+          }
+        }
+        while (true) {
+          const uint64_t bal = __ballot(flags != 0);
+          if (bal == 0) break;
+          const int L = __ffsll((unsigned long long)bal) - 1;
+          const uint32_t fl = __shfl(flags, L);
+          const int r = __ffs(fl) - 1;
+          const int gi = 1024 * j + 16 * L + r;   // coordinate of pass-2 element r of lane L
+          const int b = gi >> LOG2H;
+          const int jj = gi & (H - 1);
+          double part = 0.0;
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) {
+            const int gk = gin(j, lane, rr);
+            if ((gk >> LOG2H) == b) {
+              double yv;
+              if (BF16) yv = (double)__uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t*>(smem + addr[rr])) << 16);
+              else yv = (double)*reinterpret_cast<const float*>(smem + addr[rr]);
+              part += (__popc(jj & gk & (H - 1)) & 1) ? -yv : yv;
+            }
+          }
+          part = wave_sum_d(part);
+          if (lane == L) {
+            const double u = part / (sqrt((double)H) * (sqrt(ss) + OQ_EPS));
+            // u is exact here: its cell holds the only threshold that can lie in it
+            const double cf = fmin(fmax(floor((u - a.g_lo) * a.g_invw), 0.0), (double)(G - 1));
+            const int2 e = lut[(int)cf];
+            const uint32_t nidx = (uint32_t)e.y + ((double)__int_as_float(e.x) < u ? 1u : 0u);
+            constexpr uint32_t mask = (1u << BITS) - 1;
+            pw[r / PER] = (pw[r / PER] & ~(mask << (BITS * (r % PER)))) | (nidx << (BITS * (r % PER)));
+            flags &= ~(1u << r);
+          }
+        }
+      }
+
+      // ---- 6. stores ----------------------------------------------------------------
+      const int64_t ob = tok * (int64_t)d + 1024 * j + 16 * lane;  // first coordinate of this slot
+      if (BITS == 4) *reinterpret_cast<uint2*>(a.x_idx + ob / 2) = make_uint2(pw[0], pw[NW - 1]);
+      else if (BITS == 2) *reinterpret_cast<uint32_t*>(a.x_idx + ob / 4) = pw[0];
+      else *reinterpret_cast<u32x4*>(a.x_idx + ob) = u32x4{pw[0], pw[1 % NW], pw[2 % NW], pw[3 % NW]};
+      if (a.x_rot) {
+        f32x4* xr = reinterpret_cast<f32x4*>(a.x_rot + ob);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          xr[k] = f32x4{y[4 * k] * inv_sqrt_h, y[4 * k + 1] * inv_sqrt_h, y[4 * k + 2] * inv_sqrt_h,
+                        y[4 * k + 3] * inv_sqrt_h};
+      }
+    }
+    if (lane == 0) a.s[tok] = s32;
+    wave_sync_lds();  // every lane's gathers are done before the next row is staged
+  }
+}
+
 // ---- weights: one workgroup per row, fp64 -----------------------------------
 template <bool BF16, int BITS>
 __global__ void __launch_bounds__(256) wq_kernel(const WqArgs a) {
@@ -486,7 +814,7 @@ hipError_t allow_lds(K kernel, bool& done) {
 }
 
 int device_cus() {
-  static int cus = 0;
+  static thread_local int cus = 0;
   if (cus == 0) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -497,7 +825,7 @@ int device_cus() {
 
 template <int LOG2H, bool BF16, int BITS>
 hipError_t rq_go(const RqArgs& a, const RqPlan& p, hipStream_t st) {
-  static bool attr = false;
+  static thread_local bool attr = false;
   hipError_t e = allow_lds(&rq_act_kernel<LOG2H, BF16, BITS>, attr);
   if (e != hipSuccess) return e;
   // persistent grid: as many workgroups as are resident at once, each looping over tokens
@@ -522,7 +850,7 @@ hipError_t rq_dispatch_bits(const RqArgs& a, int bits, const RqPlan& p, hipStrea
 
 template <bool BF16, int BITS>
 hipError_t wq_go(const WqArgs& a, size_t lds, hipStream_t st) {
-  static bool attr = false;
+  static thread_local bool attr = false;
   hipError_t e = allow_lds(&wq_kernel<BF16, BITS>, attr);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((wq_kernel<BF16, BITS>), dim3(a.d_out), dim3(256), lds, st, a);
@@ -544,11 +872,83 @@ hipError_t rq_dispatch(const RqArgs& a, int bits, const RqPlan& p, hipStream_t s
   }
 }
 
+template <int LOG2H, bool BF16, int BITS, int J>
+hipError_t rqw_go(const RqArgs& a, const RqPlan& p, hipStream_t st) {
+  static thread_local bool attr = false;
+  hipError_t e = allow_lds(&rq_wave_kernel<LOG2H, BF16, BITS, J>, attr);
+  if (e != hipSuccess) return e;
+  // resident workgroups per CU, cached per (threads, LDS bytes) of this instantiation
+  static thread_local int per_cu = 0, c_threads = 0;
+  static thread_local size_t c_lds = 0;
+  if (per_cu == 0 || c_threads != p.threads || c_lds != p.lds) {
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, rq_wave_kernel<LOG2H, BF16, BITS, J>, p.threads, p.lds);
+    if (e != hipSuccess) return e;
+    c_threads = p.threads;
+    c_lds = p.lds;
+  }
+  const int64_t resident = (int64_t)(per_cu > 0 ? per_cu : 1) * device_cus();
+  const int grid = (int)(p.grid < resident ? p.grid : resident);
+  hipLaunchKernelGGL((rq_wave_kernel<LOG2H, BF16, BITS, J>), dim3(grid), dim3(p.threads), p.lds, st, a, p.wpb);
+  return hipGetLastError();
+}
+
+template <int LOG2H, bool BF16, int BITS>
+hipError_t rqw_dispatch_j(const RqArgs& a, const RqPlan& p, hipStream_t st) {
+  switch (p.wave_j) {
+    case 1: return rqw_go<LOG2H, BF16, BITS, 1>(a, p, st);
+    case 2: return rqw_go<LOG2H, BF16, BITS, 2>(a, p, st);
+    case 3:
+      if constexpr (BF16) return rqw_go<LOG2H, BF16, BITS, 3>(a, p, st);
+      else return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <bool BF16>
+hipError_t rqw_dispatch(const RqArgs& a, int bits, const RqPlan& p, hipStream_t st) {
+  auto by_bits = [&](auto lg) -> hipError_t {
+    constexpr int LG = decltype(lg)::value;
+    switch (bits) {
+      case 2: return rqw_dispatch_j<LG, BF16, 2>(a, p, st);
+      case 4: return rqw_dispatch_j<LG, BF16, 4>(a, p, st);
+      case 8: return rqw_dispatch_j<LG, BF16, 8>(a, p, st);
+      default: return hipErrorInvalidValue;
+    }
+  };
+  switch (a.log2h) {
+    case 6: return by_bits(std::integral_constant<int, 6>{});
+    case 8: return by_bits(std::integral_constant<int, 8>{});
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
 
 bool rq_plan(int32_t d, int32_t log2h, bool bf16, int64_t T, int G, RqPlan* p) {
   if (log2h < 1 || log2h > 8 || d % 16 != 0 || d % (1 << log2h) != 0) return false;
   const int ns = d / 16;
+  p->wave_j = 0;
+  p->wpb = 0;
+  // one wavefront per token: d = 1024 J with J <= 3 (bf16) or J <= 2 (fp32: the
+  // prefetched row takes twice the registers), h in {64, 256}, grid search
+  if (ns % 64 == 0 && ns / 64 <= (bf16 ? 3 : 2) && (log2h == 6 || log2h == 8) && G > 0) {
+    const int J = ns / 64;
+    const int es = bf16 ? 2 : 4;
+    int wpb = 12;   // 768 threads: 3 wavefronts per SIMD (the kernel's register budget)
+    while (wpb > 4 && rqw_layout(d, log2h, es, G, wpb).total > 160 * 1024) wpb -= 4;
+    const RqwLayout L = rqw_layout(d, log2h, es, G, wpb);
+    if (L.total <= 160 * 1024) {
+      p->ns = ns;
+      p->tpw = 1;
+      p->wave_j = J;
+      p->wpb = wpb;
+      p->threads = 64 * wpb;
+      p->lds = L.total;
+      const int64_t groups = (T + wpb - 1) / wpb;
+      p->grid = (int)(groups < (1 << 30) ? (groups > 0 ? groups : 1) : (1 << 30));
+      return true;
+    }
+  }
   int tpw;
   if (ns % 64 == 0 && ns <= 768) tpw = 1;
   else if (ns < 64 && (ns & (ns - 1)) == 0) tpw = 256 / ns;
@@ -565,6 +965,7 @@ bool rq_plan(int32_t d, int32_t log2h, bool bf16, int64_t T, int G, RqPlan* p) {
 }
 
 hipError_t rq_launch(const RqArgs& a, bool bf16, int bits, const RqPlan& p, hipStream_t st) {
+  if (p.wave_j > 0) return bf16 ? rqw_dispatch<true>(a, bits, p, st) : rqw_dispatch<false>(a, bits, p, st);
   return bf16 ? rq_dispatch<true>(a, bits, p, st) : rq_dispatch<false>(a, bits, p, st);
 }
 
