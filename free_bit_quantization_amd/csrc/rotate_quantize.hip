@@ -489,7 +489,7 @@ __global__ void __launch_bounds__(768) rq_wave_kernel(const RqArgs a, const int 
   unsigned char* wrow = smem + Ly.wave0 + (size_t)wave * Ly.wave_bytes;   // this wavefront's row
   float* wtr = reinterpret_cast<float*>(wrow + Ly.row_bytes);           // and transpose buffer
 
-  // raw chunks l + 64 i of the first token, requested before the set-up
+  // raw chunks l + 64 i of this wavefront's current token
   u32x4 raw[J][NV];
   auto fetch = [&](int64_t tok) {
     tok = tok < T ? tok : T - 1;
@@ -501,42 +501,38 @@ __global__ void __launch_bounds__(768) rq_wave_kernel(const RqArgs a, const int 
       for (int k = 0; k < NV; ++k) raw[i][k] = src[k];
     }
   };
-  if (gw < T) fetch(gw);
-
   // ---- set-up: thresholds, grid, sign masks, gather addresses ---------------
-  for (int i = tid; i < 256; i += blockDim.x) thr[i] = i < nthr ? a.thr[i] : INFINITY;
-  int8_t* sp = reinterpret_cast<int8_t*>(smem + Ly.wave0);   // sign' scratch over the wave buffers
-  {
-    // d <= 4096 and blockDim >= 256: at most 16 entries per thread
-    int pj[16];
-    int8_t sj[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int i = tid + k * (int)blockDim.x;
-      pj[k] = i < d ? (int)min((unsigned)a.perm[i], (unsigned)(d - 1)) : 0;  // perm is a permutation
-      sj[k] = i < d ? a.sign[i] : 0;
-    }
-#pragma unroll
-    for (int k = 0; k < 16; ++k)
-      if (tid + k * (int)blockDim.x < d) sp[pj[k]] = sj[k];
-  }
+  // The small set-up loads (perm, sign: cache-resident after the first
+  // workgroup) are issued before the first token's row, so they do not queue
+  // behind it; the row streams in while the tables are built.
   // pass-1 element r of slot j of lane l has coordinate gin(j, l, r); its row
   // offset perm(gin) * ES sits at atab[((4 j + r / 4) * 64 + l) * 4 + r % 4], so
   // a slot's 16 offsets are four conflict-free 16-byte reads per lane
   auto gin = [&](int j, int l, int r) { return 1024 * j + (l / BL) * H + r * BL + (l % BL); };
+  // d <= 4096 and blockDim >= 256: at most 16 entries per thread
+  int pj[16], pa[16];
+  int8_t sj[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int i = tid + k * (int)blockDim.x;
+    pj[k] = i < d ? (int)min((unsigned)a.perm[i], (unsigned)(d - 1)) : 0;  // perm is a permutation
+    sj[k] = i < d ? a.sign[i] : 0;
+    const int kk = i & 3, l = (i >> 2) & 63, jq = i >> 8;   // table entry i: ((4 j + q) * 64 + l) * 4 + kk
+    pa[k] = i < d ? (int)min((unsigned)a.perm[gin(jq >> 2, l, 4 * (jq & 3) + kk)], (unsigned)(d - 1)) : 0;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if (gw < T) fetch(gw);
+  __builtin_amdgcn_sched_barrier(0);
+
+  for (int i = tid; i < 256; i += blockDim.x) thr[i] = i < nthr ? a.thr[i] : INFINITY;
+  int8_t* sp = reinterpret_cast<int8_t*>(smem + Ly.wave0);   // sign' scratch over the wave buffers
   uint32_t* atab = reinterpret_cast<uint32_t*>(smem + Ly.atab);
-  {
-    int pj[16];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int e = tid + k * (int)blockDim.x;   // table entry: ((4 j + q) * 64 + l) * 4 + kk
-      const int kk = e & 3, l = (e >> 2) & 63, jq = e >> 8;
-      pj[k] = e < d ? (int)min((unsigned)a.perm[gin(jq >> 2, l, 4 * (jq & 3) + kk)], (unsigned)(d - 1)) : 0;
-    }
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int e = tid + k * (int)blockDim.x;
-      if (e < d) atab[e] = (uint32_t)pj[k] * ES;
+  for (int k = 0; k < 16; ++k) {
+    const int i = tid + k * (int)blockDim.x;
+    if (i < d) {
+      sp[pj[k]] = sj[k];
+      atab[i] = (uint32_t)pa[k] * ES;
     }
   }
   __syncthreads();
