@@ -10,7 +10,9 @@ the activation batches rotate through a ring of buffers larger than the
 256 MB Infinity Cache so the rotate-quantize kernel reads from HBM.
 
 Prints one JSON line.  Per-kernel durations come from HIP events recorded
-on the launch stream around every kernel of the timed steps.
+on the launch stream around every kernel of the timed steps.  With --sweep it
+prints one line per linear of every workload instead (throughput and roofline
+fractions only).
 """
 
 from __future__ import annotations
@@ -81,31 +83,13 @@ def cpu_baseline(lin, x, Wm, perm, sign, c_a, th_a, c_w, th_w, target_s: float =
             "tokens_per_s": n * reps / t}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="flux_qkv_w4a4")
-    ap.add_argument("--ring-mb", type=float, default=640.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (the layer is "
-              "token-parallel; see the sharding design notes). Run with --gpus 1.", file=sys.stderr)
-        sys.exit(2)
-
-    import numpy as np
+def measure_linear(lin, index, steps, warmup, ring_mb, dev):
+    """Time rotate-quantize + codebook GEMM of one linear (inputs resident in HBM)."""
     import torch
-
     from free_bit_quantization_amd import oq, synth
 
-    torch.cuda.set_device(0)
-    dev = torch.device("cuda:0")
-    wl = synth.workloads()[args.workload]
-    lin = wl.linears[0]
     T, K, N, h = lin.T, lin.d_in, lin.d_out, lin.h
-    x, Wm = synth.gen_linear(lin, 0, 0)
+    x, Wm = synth.gen_linear(lin, 0, index)
     perm, sign = oq.oq_build_rpbh(K, h, 0)
     c_a, th_a, _ = oq.oq_lloyd_max(K, lin.bits_a)
     c_w, th_w, _ = oq.oq_lloyd_max(K, lin.bits_w)
@@ -119,49 +103,104 @@ def main():
     del Wd
 
     # ring of activation batches (distinct buffers) larger than the Infinity Cache
-    nring = max(1, math.ceil(args.ring_mb * 1e6 / (xt.numel() * xt.element_size())))
-    ring = [torch.roll(xt, shifts=i * 7, dims=0).contiguous() for i in range(nring)]
+    nring = max(1, math.ceil(ring_mb * 1e6 / (xt.numel() * xt.element_size())))
+    ring = [xt] + [torch.roll(xt, shifts=i * 7, dims=0).contiguous() for i in range(1, nring)]
     x_idx = torch.empty((T, K * lin.bits_a // 8), dtype=torch.uint8, device=dev)
     s = torch.empty(T, dtype=torch.float32, device=dev)
     y = torch.empty((T, N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
+    epi = oq.OQ_EPI_GELU_ERF if lin.epilogue == "gelu" else oq.OQ_EPI_NONE
 
     def step(i):
         oq.oq_rotate_quantize_act(ring[i % nring], h, pd, sd, th_a, lin.bits_a, x_idx=x_idx, s=s, stream=stream)
-        oq.oq_qlinear(x_idx, s, w_idx, w_norm, K, c_a, lin.bits_a, c_w, lin.bits_w, y=y, stream=stream)
+        oq.oq_qlinear(x_idx, s, w_idx, w_norm, K, c_a, lin.bits_a, c_w, lin.bits_w, epilogue=epi, y=y,
+                      stream=stream)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         e = ev[i]
         e[0].record(stream)
         oq.oq_rotate_quantize_act(ring[i % nring], h, pd, sd, th_a, lin.bits_a, x_idx=x_idx, s=s, stream=stream)
         e[1].record(stream)
-        oq.oq_qlinear(x_idx, s, w_idx, w_norm, K, c_a, lin.bits_a, c_w, lin.bits_w, y=y, stream=stream)
+        oq.oq_qlinear(x_idx, s, w_idx, w_norm, K, c_a, lin.bits_a, c_w, lin.bits_w, epilogue=epi, y=y,
+                      stream=stream)
         e[2].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
 
     total_ms = start.elapsed_time(end)
-    ms_step = total_ms / args.steps
-    t_rq = sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps
-    t_ql = sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps
-
+    ms_step = total_ms / steps
+    t_rq = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
+    t_ql = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
     es = xt.element_size()
     rq_bytes = T * K * es + T * K * lin.bits_a // 8 + 4 * T       # read x, write indices and s
     flops = 2.0 * T * K * N
-    rq_gbs = rq_bytes / (t_rq * 1e-3) / 1e9
-    ql_tflops = flops / (t_ql * 1e-3) / 1e12
-    value = flops / (ms_step * 1e-3) / 1e12
+    r = dict(T=T, K=K, N=N, h=h, es=es, nring=nring, ms_step=ms_step, t_rq=t_rq, t_ql=t_ql, t_wall=t_wall,
+             rq_bytes=rq_bytes, flops=flops, rq_gbs=rq_bytes / (t_rq * 1e-3) / 1e9,
+             ql_tflops=flops / (t_ql * 1e-3) / 1e12, value=flops / (ms_step * 1e-3) / 1e12,
+             inputs=(x, Wm, perm, sign, c_a, th_a, c_w, th_w))
+    return r
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="flux_qkv_w4a4")
+    ap.add_argument("--ring-mb", type=float, default=640.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="one line per linear of every workload (tokens/s, GB/s, TFLOP/s, roofline fractions)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (the layer is "
+              "token-parallel; see the sharding design notes). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from free_bit_quantization_amd import synth
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+
+    if args.sweep:
+        for name in synth.WORKLOAD_ORDER:
+            for k, lin in enumerate(synth.workloads()[name].linears):
+                r = measure_linear(lin, k, args.steps, args.warmup, args.ring_mb, dev)
+                print(json.dumps({
+                    "workload": name, "linear": lin.name, "tokens": r["T"], "d_in": r["K"], "d_out": r["N"],
+                    "h": r["h"], "bits_w": lin.bits_w, "bits_a": lin.bits_a, "act_dtype": lin.act_dtype,
+                    "epilogue": lin.epilogue, "tokens_per_s": round(r["T"] / (r["ms_step"] * 1e-3), 1),
+                    "ms_per_step": round(r["ms_step"], 5),
+                    "qlinear_TFLOPs": round(r["ql_tflops"], 2), "qlinear_ms": round(r["t_ql"], 5),
+                    "qlinear_frac_fp16_peak": round(r["ql_tflops"] / FP16_MFMA_PEAK_TFLOPS, 4),
+                    "rotate_quant_GBps": round(r["rq_gbs"], 1), "rotate_quant_ms": round(r["t_rq"], 5),
+                    "rotate_quant_frac_hbm": round(r["rq_gbs"] / HBM_PEAK_GBS, 4)}), flush=True)
+                del r
+                torch.cuda.empty_cache()
+        return
+
+    wl = synth.workloads()[args.workload]
+    lin = wl.linears[0]
+    r = measure_linear(lin, 0, args.steps, args.warmup, args.ring_mb, dev)
+    T, K, N, h = r["T"], r["K"], r["N"], r["h"]
+    es, rq_bytes, flops = r["es"], r["rq_bytes"], r["flops"]
+    ms_step, t_rq, t_ql = r["ms_step"], r["t_rq"], r["t_ql"]
+    rq_gbs, ql_tflops, value = r["rq_gbs"], r["ql_tflops"], r["value"]
+    nring, t_wall = r["nring"], r["t_wall"]
+    x, Wm, perm, sign, c_a, th_a, c_w, th_w = r["inputs"]
 
     line = {
         "metric": "qlinear TFLOP/s + rotate-quant GB/s (frac of roofline), FLUX 3072-wide W4A4",
@@ -192,7 +231,7 @@ def main():
                                   "unit": "GB/s", "frac": round(rq_gbs / HBM_PEAK_GBS, 4),
                                   "traffic": traffic_of("free_bit_quantization_amd/csrc/rotate_quantize.hip"),
                                   "traffic_unit": "bytes",
-                                  "kernel": "oq_rotate_quantize_act (rq_act_kernel<8,bf16,4>)",
+                                  "kernel": "oq_rotate_quantize_act (rq_wave_kernel<8,bf16,4,3>)",
                                   "algorithmic": f"T*(K*{es} + K*{lin.bits_a}/8 + 4) = {rq_bytes} B"},
         "wall_s_timed": round(t_wall, 4),
     }
