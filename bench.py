@@ -34,8 +34,8 @@ FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, TFLOP/s
 # bench (FETCH_SIZE x 2, WRITE_SIZE x 1: the copy-kernel calibration), valid only
 # for the kernel source they were taken on (sha256 prefix); otherwise null.
 MEASURED_TRAFFIC = {
-    "free_bit_quantization_amd/csrc/qlinear.hip": ("845765ad6b0b823b", 125.7e6, 169.9e6),
-    "free_bit_quantization_amd/csrc/rotate_quantize.hip": ("4854a2d20dbcd21d", 28.7e6, 7.2e6),
+    "free_bit_quantization_amd/csrc/qlinear.hip": ("f3cab77c4b727af7", 125.7e6, 169.9e6),
+    "free_bit_quantization_amd/csrc/rotate_quantize.hip": ("a7c5edf9fe070703", 28.8e6, 7.2e6),
 }
 
 
