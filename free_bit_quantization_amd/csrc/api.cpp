@@ -74,6 +74,15 @@ oq_status oq_build_rpbh(int32_t d, int32_t h, uint64_t seed, int32_t* perm, int8
   return ok();
 }
 
+oq_status oq_build_block_rht(int32_t d, int32_t h, uint64_t seed, int32_t* perm, int8_t* sign) {
+  if (d < 2) return fail(OQ_EINVAL, "d must be >= 2 (got %d)", d);
+  if (log2_exact(h) < 0) return fail(OQ_EINVAL, "h must be a power of two >= 2 (got %d)", h);
+  if (d % h != 0) return fail(OQ_EINVAL, "h (%d) must divide d (%d)", h, d);
+  if (!perm || !sign) return fail(OQ_EINVAL, "perm / sign is NULL");
+  oq::build_block_rht_tables(d, seed, perm, sign);
+  return ok();
+}
+
 oq_status oq_lloyd_max(int32_t d, int32_t bits, double* centroids, double* thresholds, double* mse) {
   if (d < 3) return fail(OQ_EINVAL, "d must be >= 3 (got %d)", d);
   if (bits < 1 || bits > 8) return fail(OQ_EINVAL, "bits must be in 1..8 (got %d)", bits);

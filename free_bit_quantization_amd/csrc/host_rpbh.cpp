@@ -40,4 +40,13 @@ void build_rpbh_tables(int32_t d, uint64_t seed, int32_t* perm, int8_t* sign) {
   for (int32_t i = 0; i < d; ++i) sign[i] = (g.next() >> 63) ? (int8_t)-1 : (int8_t)1;
 }
 
+// Block-RHT, the rotation-ablation variant (same page, ablation paragraph:
+// RPBH without its leading permutation): identity permutation, and the signs
+// drawn from the start of the same stream (no shuffle draws before them).
+void build_block_rht_tables(int32_t d, uint64_t seed, int32_t* perm, int8_t* sign) {
+  SplitMix64 g{seed};
+  for (int32_t i = 0; i < d; ++i) perm[i] = i;
+  for (int32_t i = 0; i < d; ++i) sign[i] = (g.next() >> 63) ? (int8_t)-1 : (int8_t)1;
+}
+
 }  // namespace oq

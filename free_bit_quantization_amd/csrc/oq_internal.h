@@ -11,6 +11,7 @@ namespace oq {
 
 // ---- host math --------------------------------------------------------------
 void build_rpbh_tables(int32_t d, uint64_t seed, int32_t* perm, int8_t* sign);
+void build_block_rht_tables(int32_t d, uint64_t seed, int32_t* perm, int8_t* sign);
 // 0 on convergence (relative fixed-point residual <= 1e-10), -1 otherwise.
 int lloyd_max_fd(int d, int bits, double* centroids, double* thresholds, double* mse, double* resid);
 

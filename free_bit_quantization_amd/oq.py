@@ -23,8 +23,8 @@ OQ_F32, OQ_BF16 = 0, 1
 OQ_EPI_NONE, OQ_EPI_GELU_ERF = 0, 1
 
 # every symbol include/oq.h declares
-EXPORTS = ("oq_last_error", "oq_version", "oq_build_rpbh", "oq_lloyd_max", "oq_quantize_weights",
-           "oq_rotate_quantize_act", "oq_qlinear")
+EXPORTS = ("oq_last_error", "oq_version", "oq_build_rpbh", "oq_build_block_rht", "oq_lloyd_max",
+           "oq_quantize_weights", "oq_rotate_quantize_act", "oq_qlinear")
 
 
 class OQError(RuntimeError):
@@ -54,6 +54,8 @@ def lib() -> ctypes.CDLL:
         L.oq_version.argtypes = []
         L.oq_build_rpbh.restype = _I32
         L.oq_build_rpbh.argtypes = [_I32, _I32, ctypes.c_uint64, _P, _P]
+        L.oq_build_block_rht.restype = _I32
+        L.oq_build_block_rht.argtypes = [_I32, _I32, ctypes.c_uint64, _P, _P]
         L.oq_lloyd_max.restype = _I32
         L.oq_lloyd_max.argtypes = [_I32, _I32, _P, _P, _P]
         L.oq_quantize_weights.restype = _I32
@@ -110,6 +112,14 @@ def oq_build_rpbh(d: int, h: int, seed: int = 0):
     perm = np.empty(d, dtype=np.int32)
     sign = np.empty(d, dtype=np.int8)
     _check(lib().oq_build_rpbh(d, h, seed, perm.ctypes.data, sign.ctypes.data))
+    return perm, sign
+
+
+def oq_build_block_rht(d: int, h: int, seed: int = 0):
+    """(perm int32[d] = identity, sign int8[d]) of the Block-RHT ablation variant."""
+    perm = np.empty(d, dtype=np.int32)
+    sign = np.empty(d, dtype=np.int8)
+    _check(lib().oq_build_block_rht(d, h, seed, perm.ctypes.data, sign.ctypes.data))
     return perm, sign
 
 

@@ -86,6 +86,18 @@ const char* oq_version(void);
 oq_status oq_build_rpbh(int32_t d, int32_t h, uint64_t seed, int32_t* perm, int8_t* sign);
 
 /*
+ * oq_build_block_rht -- the rotation-ablation variant of the same page
+ * (rcap.io summary, ablation paragraph: RPBH without its leading uniform
+ * permutation, "Block-RHT"): perm[i] = i, and sign[i] = -1 if the top bit of
+ * the (i+1)-th output of splitmix64(seed) is set, else +1 (the sign draws of
+ * oq_build_rpbh without the shuffle draws before them).  The tables feed the
+ * same kernels as RPBH tables (oq_quantize_weights, oq_rotate_quantize_act).
+ *
+ * Arguments and errors as oq_build_rpbh.
+ */
+oq_status oq_build_block_rht(int32_t d, int32_t h, uint64_t seed, int32_t* perm, int8_t* sign);
+
+/*
  * oq_lloyd_max -- codebook[d, b] of the offline pseudo-code: the Lloyd-Max
  * quantizer (rcap.io summary, "core trick" paragraph) with L = 2^bits levels
  * for the exact marginal f_d(t) = C_d (1 - t^2)^((d-3)/2) on [-1, 1] of one

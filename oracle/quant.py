@@ -53,6 +53,21 @@ def quantize_activations(X, perm, sign, h, thresholds, eps: float = EPS):
     return nearest_index(u, thresholds), s, x_rot, u
 
 
+def quantize_rotated(x_rot, thresholds, eps: float = EPS):
+    """The same norm / normalise / nearest-centroid step for rows already
+    rotated by any orthogonal R (the dense reference rotation of the page's
+    RPBH paragraph, or a variant): returns (idx[T, d], s[T])."""
+    s = np.linalg.norm(x_rot, axis=1)
+    return nearest_index(x_rot / (s + eps)[:, None], thresholds), s
+
+
+def relative_error(x_rot, idx, s, centroids) -> float:
+    """||s c[idx] - x_rot||_F / ||x_rot||_F: the quantization error of the
+    rows; R is orthogonal, so it is also the error in the original basis."""
+    xq = np.asarray(s)[:, None] * np.asarray(centroids)[idx]
+    return float(np.linalg.norm(xq - x_rot) / np.linalg.norm(x_rot))
+
+
 def quantize_weights(W, perm, sign, h, thresholds, eps: float = EPS):
     """Offline step per weight matrix: returns (idx[N, d], norms[N], W_rot, u)."""
     w_rot = rotate(W, perm, sign, h)

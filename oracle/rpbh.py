@@ -64,6 +64,33 @@ def build_rpbh(d: int, h: int, seed: int):
     return np.asarray(perm, dtype=np.int64), np.asarray(sign, dtype=np.int8)
 
 
+def build_block_rht(d: int, h: int, seed: int):
+    """Block-RHT, the ablation variant without the leading permutation.
+
+    Same page, ablation paragraph (removing RPBH's uniform permutation).
+    Reading: perm is the identity and the signs are the first d draws of the
+    same splitmix64 stream (the RPBH sign rule without the shuffle draws).
+    """
+    if d <= 0 or h < 2 or (h & (h - 1)) != 0 or d % h != 0:
+        raise ValueError(f"invalid Block-RHT shape d={d} h={h}")
+    rng = SplitMix64(seed)
+    sign = [(-1 if (rng.next() >> 63) else 1) for _ in range(d)]
+    return np.arange(d, dtype=np.int64), np.asarray(sign, dtype=np.int8)
+
+
+def haar_rotation(d: int, seed: int) -> np.ndarray:
+    """A dense Haar-random orthogonal d x d matrix (fp64): QR of a Gaussian
+    matrix with the signs of R's diagonal moved into Q (Mezzadri, "How to
+    generate random matrices from the classical compact groups", 2007).
+
+    The page's reference point for RPBH: a dense random rotation, O(d^2) per
+    token, which RPBH replaces (paragraph on the RPBH rotation).
+    """
+    g = np.random.default_rng(np.random.SeedSequence([seed, d]))
+    q, r = np.linalg.qr(g.standard_normal((d, d)))
+    return q * np.sign(np.diag(r))
+
+
 def sylvester(h: int) -> np.ndarray:
     """Unnormalised Sylvester-Hadamard matrix, H[i, j] = (-1)^popcount(i & j)."""
     i = np.arange(h)

@@ -77,21 +77,27 @@ def to_device(x: np.ndarray, dtype: str):
     return t.cuda()
 
 
-def rotation(d: int, h: int, seed: int = 0):
+def rotation(d: int, h: int, seed: int = 0, kind: str = "rpbh"):
+    """Library rotation tables (checked bit-identical to the oracle's), host and device.
+    kind: "rpbh" or "block_rht" (the ablation variant without the permutation)."""
     import torch
-    perm, sign = oq.oq_build_rpbh(d, h, seed)
-    po, so = rpbh.build_rpbh(d, h, seed)
+    if kind == "rpbh":
+        perm, sign = oq.oq_build_rpbh(d, h, seed)
+        po, so = rpbh.build_rpbh(d, h, seed)
+    else:
+        perm, sign = oq.oq_build_block_rht(d, h, seed)
+        po, so = rpbh.build_block_rht(d, h, seed)
     assert np.array_equal(perm, po) and np.array_equal(sign, so)
     return perm, sign, torch.from_numpy(perm).cuda(), torch.from_numpy(sign).cuda()
 
 
 def check_activations(x: np.ndarray, dtype: str, h: int, bits: int, seed: int = 0, rows: Optional[np.ndarray] = None,
-                      want_x_rot: bool = True, name: str = ""):
+                      want_x_rot: bool = True, name: str = "", kind: str = "rpbh"):
     """rotate-quantize x on the GPU; compare rows (all if None) with the oracle.
 
     Returns (x_idx device tensor, s device tensor, report dict)."""
     T, d = x.shape
-    perm, sign, pd, sd = rotation(d, h, seed)
+    perm, sign, pd, sd = rotation(d, h, seed, kind)
     cb = library_codebook(d, bits)
     xd = to_device(x, dtype)
     x_idx, s, x_rot = oq.oq_rotate_quantize_act(xd, h, pd, sd, cb.th, bits, want_x_rot=want_x_rot)
@@ -115,10 +121,10 @@ def check_activations(x: np.ndarray, dtype: str, h: int, bits: int, seed: int = 
     return x_idx, s, rep
 
 
-def check_weights(W: np.ndarray, h: int, bits: int, seed: int = 0, name: str = ""):
+def check_weights(W: np.ndarray, h: int, bits: int, seed: int = 0, name: str = "", kind: str = "rpbh"):
     """Quantize W on the GPU (fp64 path); indices must be bit-exact."""
     d_out, d = W.shape
-    perm, sign, pd, sd = rotation(d, h, seed)
+    perm, sign, pd, sd = rotation(d, h, seed, kind)
     cb = library_codebook(d, bits)
     Wd = to_device(W, "f32")
     w_idx, w_norm = oq.oq_quantize_weights(Wd, h, pd, sd, cb.th, bits)

@@ -43,15 +43,15 @@ def _assert_gemm(rep):
 
 
 def run_linear(lin, index=0, T=None, seed=0, bias=False, act_rows=None, gemm_rows=None, x=None, W_=None,
-               x_dtype=None):
+               x_dtype=None, kind="rpbh"):
     P.log(f"== linear {lin.name} T={T or lin.T} K={lin.d_in} N={lin.d_out} W{lin.bits_w}A{lin.bits_a}")
     xg, Wg = synth.gen_linear(lin, seed, index, T=T, need_act=x is None)
     x = xg if x is None else x
     W_ = Wg if W_ is None else W_
     x_idx, s, ra = P.check_activations(x, x_dtype or lin.act_dtype, lin.h, lin.bits_a, rows=act_rows,
-                                       want_x_rot=True, name=lin.name)
+                                       want_x_rot=True, name=lin.name, kind=kind)
     _assert_act(ra)
-    w_idx, w_norm, rw = P.check_weights(W_, lin.h, lin.bits_w, name=lin.name)
+    w_idx, w_norm, rw = P.check_weights(W_, lin.h, lin.bits_w, name=lin.name, kind=kind)
     _assert_w(rw)
     b = synth.gen_bias(lin.d_out, seed) if bias else None
     y, rg = P.check_gemm(x_idx, s, w_idx, w_norm, lin.d_in, lin.bits_a, lin.bits_w, bias=b,
@@ -92,6 +92,14 @@ def test_wan_ffn_prefix_ragged():
 def test_flux_block_w4a8_prefix(k):
     lin = W["flux_block_w4a8_b2"].linears[k]
     run_linear(lin, index=k, T=136 if lin.T > 1024 else 72)
+
+
+# ---- rotation variant (ablation without the permutation): same kernels, other tables
+
+
+def test_block_rht_tables_through_both_kernels():
+    run_linear(W["flux_qkv_w4a4"].linears[0], T=200, kind="block_rht")
+    run_linear(W["single_w4a4_64x256x256"].linears[0], kind="block_rht")
 
 
 # ---- edge cases ----------------------------------------------------------------

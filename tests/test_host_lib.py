@@ -33,6 +33,14 @@ def test_rpbh_bit_identical_to_oracle(d, h, seed):
     np.testing.assert_array_equal(s, so)
 
 
+@pytest.mark.parametrize("d,h,seed", [(8, 2, 0), (256, 64, 0), (3072, 256, 0), (5120, 256, 0), (12288, 256, 0), (96, 32, 77)])
+def test_block_rht_bit_identical_to_oracle(d, h, seed):
+    p, s = oq.oq_build_block_rht(d, h, seed)
+    po, so = rpbh.build_block_rht(d, h, seed)
+    np.testing.assert_array_equal(p, po)
+    np.testing.assert_array_equal(s, so)
+
+
 @pytest.mark.parametrize("d,bits", [(3, 2), (256, 1), (256, 4), (3072, 2), (3072, 4), (3072, 8), (5120, 4),
                                     (12288, 2), (12288, 4), (12288, 8)])
 def test_lloyd_max_agrees_with_oracle(d, bits):
@@ -53,6 +61,9 @@ def test_host_argument_errors():
     assert L.oq_build_rpbh(8, 3, 0, perm.ctypes.data, sign.ctypes.data) == oq.OQ_EINVAL
     assert L.oq_build_rpbh(8, 16, 0, perm.ctypes.data, sign.ctypes.data) == oq.OQ_EINVAL
     assert L.oq_build_rpbh(8, 2, 0, None, sign.ctypes.data) == oq.OQ_EINVAL
+    assert L.oq_build_block_rht(8, 3, 0, perm.ctypes.data, sign.ctypes.data) == oq.OQ_EINVAL
+    assert L.oq_build_block_rht(8, 16, 0, perm.ctypes.data, sign.ctypes.data) == oq.OQ_EINVAL
+    assert L.oq_build_block_rht(8, 2, 0, perm.ctypes.data, None) == oq.OQ_EINVAL
     assert b"NULL" in L.oq_last_error()
     c = np.zeros(16)
     t = np.zeros(15)
