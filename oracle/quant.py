@@ -26,7 +26,10 @@ Readings:
   is s itself.  The same guard divides weight rows by (n + eps).
 * the codebook is for d = d_in (one codebook per input dimension), not h.
 * index 0 is the most negative centroid; packing is row-major, K-contiguous,
-  least-significant bits first within each byte (2, 4 or 8 bits).
+  least-significant bits first: a row is a little-endian bit stream, index k
+  in bits [k b, (k+1) b) (for 2, 4, 8 bits: LSB first within each byte; the
+  pages name 3- and 6-bit widths without a layout, this is its plainest
+  extension).
 * GELU for the MLP chain is the exact erf form, 0.5 y (1 + erf(y / sqrt 2)).
 """
 
@@ -77,26 +80,26 @@ def quantize_weights(W, perm, sign, h, thresholds, eps: float = EPS):
 
 
 def pack(idx: np.ndarray, bits: int) -> np.ndarray:
-    """Pack [R, K] indices (< 2^bits) into [R, K*bits/8] bytes, LSB first."""
+    """Pack [R, K] indices (< 2^bits, 1 <= bits <= 8) into [R, K*bits/8]
+    bytes: each row is a little-endian bit stream in which index k occupies
+    bits [k*bits, (k+1)*bits) and byte j holds bits [8j, 8j+8).  For 2, 4
+    and 8 bits this is "LSB first within each byte"."""
     idx = np.asarray(idx, dtype=np.int64)
     R, K = idx.shape
-    per = 8 // bits
-    if K % per:
-        raise ValueError("K must fill whole bytes")
-    g = idx.reshape(R, K // per, per)
-    out = np.zeros((R, K // per), dtype=np.int64)
-    for k in range(per):
-        out |= g[:, :, k] << (k * bits)
-    return out.astype(np.uint8)
+    if not 1 <= bits <= 8 or (K * bits) % 8:
+        raise ValueError("need 1 <= bits <= 8 and K * bits a whole number of bytes")
+    if idx.size and (idx.min() < 0 or idx.max() >= (1 << bits)):
+        raise ValueError("index out of range")
+    stream = ((idx[:, :, None] >> np.arange(bits)) & 1).astype(np.uint8).reshape(R, K * bits)
+    return np.packbits(stream, axis=1, bitorder="little")
 
 
 def unpack(packed: np.ndarray, bits: int, K: int) -> np.ndarray:
     """Inverse of :func:`pack`."""
-    p = np.asarray(packed, dtype=np.int64)
-    per = 8 // bits
-    mask = (1 << bits) - 1
-    out = np.stack([(p >> (k * bits)) & mask for k in range(per)], axis=-1)
-    return out.reshape(p.shape[0], -1)[:, :K]
+    p = np.asarray(packed, dtype=np.uint8)
+    R = p.shape[0]
+    stream = np.unpackbits(p, axis=1, bitorder="little")[:, :K * bits].astype(np.int64)
+    return (stream.reshape(R, K, bits) << np.arange(bits)).sum(axis=2)
 
 
 def gelu_erf(y):

@@ -34,9 +34,15 @@ def test_pack_layout_by_hand():
     np.testing.assert_array_equal(quant.pack(idx2, 2), [[0b00111001, 0xFF]])
     idx8 = np.array([[0, 255, 17]])
     np.testing.assert_array_equal(quant.pack(idx8, 8), [[0, 255, 17]])
+    # 3 bits: sum_k idx_k << 3k = 0x1F58D1, little-endian bytes
+    idx3 = np.array([[1, 2, 3, 4, 5, 6, 7, 0]])
+    np.testing.assert_array_equal(quant.pack(idx3, 3), [[0xD1, 0x58, 0x1F]])
+    # 6 bits: 1 + 63 << 6 + 32 << 12 + 5 << 18 = 0x160FC1
+    idx6 = np.array([[1, 63, 32, 5]])
+    np.testing.assert_array_equal(quant.pack(idx6, 6), [[0xC1, 0x0F, 0x16]])
 
 
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_pack_roundtrip(bits):
     rng = np.random.default_rng(bits)
     idx = rng.integers(0, 1 << bits, size=(7, 64))
