@@ -36,7 +36,7 @@ int log2_exact(int32_t h) {
   return m;
 }
 
-bool bits_ok(int32_t b) { return b == 2 || b == 4 || b == 8; }
+bool bits_ok(int32_t b) { return b == 2 || b == 3 || b == 4 || b == 6 || b == 8; }
 
 // Thresholds must be finite and strictly increasing, also after rounding to fp32.
 oq_status check_thresholds(const double* th, int n, bool need_f32) {
@@ -100,7 +100,7 @@ oq_status oq_quantize_weights(const void* W, oq_dtype w_dtype, int32_t d_out, in
   if (w_dtype != OQ_F32 && w_dtype != OQ_BF16) return fail(OQ_EINVAL, "w_dtype must be OQ_F32 or OQ_BF16");
   if (d_out < 0) return fail(OQ_EINVAL, "d_out must be >= 0");
   if (d_in < 2 || m < 0 || d_in % h != 0) return fail(OQ_EINVAL, "need h a power of two >= 2 dividing d_in");
-  if (!bits_ok(bits_w)) return fail(OQ_EINVAL, "bits_w must be 2, 4 or 8 (got %d)", bits_w);
+  if (!bits_ok(bits_w)) return fail(OQ_EINVAL, "bits_w must be 2, 3, 4, 6 or 8 (got %d)", bits_w);
   if ((d_in * bits_w) % 8 != 0) return fail(OQ_EINVAL, "d_in * bits_w must fill whole bytes");
   const int nthr = (1 << bits_w) - 1;
   oq_status st = check_thresholds(thresholds, nthr, false);
@@ -126,7 +126,7 @@ oq_status oq_rotate_quantize_act(const void* x, oq_dtype x_dtype, int64_t T, int
   if (T < 0) return fail(OQ_EINVAL, "T must be >= 0");
   if (d < 16 || d % 16 != 0) return fail(OQ_EINVAL, "d must be a positive multiple of 16 (got %d)", d);
   if (m < 0 || d % h != 0) return fail(OQ_EINVAL, "need h a power of two >= 2 dividing d");
-  if (!bits_ok(bits_a)) return fail(OQ_EINVAL, "bits_a must be 2, 4 or 8 (got %d)", bits_a);
+  if (!bits_ok(bits_a)) return fail(OQ_EINVAL, "bits_a must be 2, 3, 4, 6 or 8 (got %d)", bits_a);
   const int nthr = (1 << bits_a) - 1;
   oq_status st = check_thresholds(thresholds, nthr, true);
   if (st != OQ_OK) return st;
@@ -177,7 +177,7 @@ oq_status oq_qlinear(const uint8_t* x_idx, const float* s, int64_t T, const uint
                      hipStream_t stream) {
   if (T < 0 || d_out < 0) return fail(OQ_EINVAL, "T and d_out must be >= 0");
   if (d_in <= 0) return fail(OQ_EINVAL, "d_in must be > 0");
-  if (!bits_ok(bits_a) || !bits_ok(bits_w)) return fail(OQ_EINVAL, "bits must be 2, 4 or 8");
+  if (!bits_ok(bits_a) || !bits_ok(bits_w)) return fail(OQ_EINVAL, "bits must be 2, 3, 4, 6 or 8");
   if (epilogue != OQ_EPI_NONE && epilogue != OQ_EPI_GELU_ERF) return fail(OQ_EINVAL, "unknown epilogue %d", epilogue);
   if (!centroids_a || !centroids_w) return fail(OQ_EINVAL, "centroids is NULL");
   const int La = 1 << bits_a, Lw = 1 << bits_w;

@@ -91,6 +91,62 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 
 __host__ __device__ inline size_t align16(size_t v) { return (v + 15) & ~size_t(15); }
 
+// Packed indices of one 16-coordinate slot: index r occupies bits
+// [r BITS, (r+1) BITS) of a little-endian stream held in 32-bit words (the
+// row layout of the index arrays); 2 BITS bytes are stored.
+template <int BITS>
+struct Pack16 {
+  static constexpr int NW = (16 * BITS + 31) / 32;
+  uint32_t w[NW];
+  __device__ __forceinline__ Pack16() {
+#pragma unroll
+    for (int k = 0; k < NW; ++k) w[k] = 0;
+  }
+  // r must be a compile-time constant after unrolling
+  __device__ __forceinline__ void put(int r, uint32_t v) {
+    const int pos = BITS * r, k = pos >> 5, sh = pos & 31;
+    w[k] |= v << sh;
+    if (sh + BITS > 32) w[k + 1] |= v >> (32 - sh);
+  }
+  // replace index r (any r): on two 64-bit halves with runtime shifts, so the
+  // words stay in registers
+  __device__ __forceinline__ void set(int r, uint32_t v) {
+    const uint64_t m = (1ull << BITS) - 1;
+    uint64_t lo = w[0], hi = 0;
+    if constexpr (NW > 1) lo |= (uint64_t)w[1] << 32;
+    if constexpr (NW > 2) hi = w[2];
+    if constexpr (NW > 3) hi |= (uint64_t)w[3] << 32;
+    const int pos = BITS * r;
+    if (pos < 64) {
+      lo = (lo & ~(m << pos)) | ((uint64_t)v << pos);
+      if (pos + BITS > 64) hi = (hi & ~(m >> (64 - pos))) | ((uint64_t)v >> (64 - pos));
+    } else {
+      hi = (hi & ~(m << (pos - 64))) | ((uint64_t)v << (pos - 64));
+    }
+    w[0] = (uint32_t)lo;
+    if constexpr (NW > 1) w[1] = (uint32_t)(lo >> 32);
+    if constexpr (NW > 2) w[2] = (uint32_t)hi;
+    if constexpr (NW > 3) w[3] = (uint32_t)(hi >> 32);
+  }
+  // p: first byte of the slot (2 BITS bytes; aligned to 2 BITS bytes' natural unit)
+  __device__ __forceinline__ void store(uint8_t* p) const {
+    if constexpr (BITS == 2) {
+      *reinterpret_cast<uint32_t*>(p) = w[0];
+    } else if constexpr (BITS == 4) {
+      *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+    } else if constexpr (BITS == 8) {
+      *reinterpret_cast<u32x4*>(p) = u32x4{w[0], w[1], w[2], w[3]};
+    } else if constexpr (BITS == 6) {   // 12 bytes, 4-byte aligned
+      uint32_t* q = reinterpret_cast<uint32_t*>(p);
+      q[0] = w[0]; q[1] = w[1]; q[2] = w[2];
+    } else {                            // 3 bits: 6 bytes, 2-byte aligned
+      static_assert(BITS == 3, "index widths 2, 3, 4, 6, 8");
+      uint16_t* q = reinterpret_cast<uint16_t*>(p);
+      q[0] = (uint16_t)w[0]; q[1] = (uint16_t)(w[0] >> 16); q[2] = (uint16_t)w[1];
+    }
+  }
+};
+
 struct RqLayout {
   size_t lut, thr, row, trans, red, total, row_stride;  // row_stride: bytes of one parity buffer
 };
@@ -313,16 +369,9 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
     }
 
     // ---- 4./5. threshold search and guard ----------------------------------------
-    uint64_t pk0 = 0, pk1 = 0;  // packed indices (pk1 only for 8-bit)
+    Pack16<BITS> pk;
     uint32_t flags = 0;
-    auto put = [&](int r, int idx) {
-      if (BITS == 8) {
-        if (r < 8) pk0 |= (uint64_t)idx << (8 * r);
-        else pk1 |= (uint64_t)idx << (8 * (r - 8));
-      } else {
-        pk0 |= (uint64_t)idx << (BITS * r);
-      }
-    };
+    auto put = [&](int r, int idx) { pk.put(r, (uint32_t)idx); };
     if (G > 0) {
       // two halves of 8: all LUT reads of a half are in flight together
 #pragma unroll
@@ -395,14 +444,7 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
       part = wave_sum_d(part);
       if (lane == L) {
         const double u = part / (sqrt((double)H) * (s64 + OQ_EPS));
-        const uint64_t nidx = (uint64_t)count_below_f64(thr, nthr, u);
-        constexpr uint64_t mask = (1ull << BITS) - 1;
-        if (BITS == 8) {
-          if (r < 8) pk0 = (pk0 & ~(mask << (8 * r))) | (nidx << (8 * r));
-          else pk1 = (pk1 & ~(mask << (8 * (r - 8)))) | (nidx << (8 * (r - 8)));
-        } else {
-          pk0 = (pk0 & ~(mask << (BITS * r))) | (nidx << (BITS * r));
-        }
+        pk.set(r, (uint32_t)count_below_f64(thr, nthr, u));
         flags &= ~(1u << r);
       }
     }
@@ -410,9 +452,7 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
     // ---- 6. stores ----------------------------------------------------------------
     if (valid) {
       const int64_t ob = tok * (int64_t)d + 16 * sl;  // first coordinate of this slot
-      if (BITS == 4) *reinterpret_cast<uint64_t*>(a.x_idx + ob / 2) = pk0;
-      else if (BITS == 2) *reinterpret_cast<uint32_t*>(a.x_idx + ob / 4) = (uint32_t)pk0;
-      else *reinterpret_cast<u64x2*>(a.x_idx + ob) = u64x2{pk0, pk1};
+      pk.store(a.x_idx + ob * BITS / 8);
       if (a.x_rot) {
         f32x4* xr = reinterpret_cast<f32x4*>(a.x_rot + ob);
 #pragma unroll
@@ -464,8 +504,6 @@ __global__ void __launch_bounds__(768) rq_wave_kernel(const RqArgs a, const int 
   static_assert(LOG2H >= 5 && LOG2H <= 8, "two-pass block sizes only");
   constexpr float kGam = 2.0f * (LOG2H + 1) * 5.9604644775390625e-8f;  // 2 (m+1) 2^-24
   constexpr float kRel = 16.0f * 5.9604644775390625e-8f;               // 16 ulp of |theta|
-  constexpr int PER = 32 / BITS;                   // indices per packed 32-bit word
-  constexpr int NW = 16 / PER;                     // packed words per slot
   constexpr int NV = BF16 ? 2 : 4;                 // 16-byte loads per 16-coordinate chunk
   constexpr int MW = BF16 ? 8 : 16;                // sign-mask words per chunk
   constexpr int d = 1024 * J;
@@ -658,9 +696,7 @@ __global__ void __launch_bounds__(768) rq_wave_kernel(const RqArgs a, const int 
 
       // ---- 4./5. grid search and guard --------------------------------------------
       const float rad = fmaf(thmax, kRel, kGam * l1 * c);
-      uint32_t pw[NW];
-#pragma unroll
-      for (int k = 0; k < NW; ++k) pw[k] = 0;
+      Pack16<BITS> pw;
       bool near = false;
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
@@ -675,7 +711,7 @@ __global__ void __launch_bounds__(768) rq_wave_kernel(const RqArgs a, const int 
           const int r = 8 * hf + q;
           const float dd = fmaf(y[r], c, -__int_as_float(e[q].x));
           const uint32_t idx = (uint32_t)e[q].y + (dd > 0.f ? 1u : 0u);
-          pw[r / PER] |= idx << (BITS * (r % PER));
+          pw.put(r, idx);
           near |= fabsf(dd) < rad;
         }
       }
@@ -718,8 +754,7 @@ __global__ void __launch_bounds__(768) rq_wave_kernel(const RqArgs a, const int 
             const double cf = fmin(fmax(floor((u - a.g_lo) * a.g_invw), 0.0), (double)(G - 1));
             const int2 e = lut[(int)cf];
             const uint32_t nidx = (uint32_t)e.y + ((double)__int_as_float(e.x) < u ? 1u : 0u);
-            constexpr uint32_t mask = (1u << BITS) - 1;
-            pw[r / PER] = (pw[r / PER] & ~(mask << (BITS * (r % PER)))) | (nidx << (BITS * (r % PER)));
+            pw.set(r, nidx);
             flags &= ~(1u << r);
           }
         }
@@ -727,9 +762,7 @@ __global__ void __launch_bounds__(768) rq_wave_kernel(const RqArgs a, const int 
 
       // ---- 6. stores ----------------------------------------------------------------
       const int64_t ob = tok * (int64_t)d + 1024 * j + 16 * lane;  // first coordinate of this slot
-      if (BITS == 4) *reinterpret_cast<uint2*>(a.x_idx + ob / 2) = make_uint2(pw[0], pw[NW - 1]);
-      else if (BITS == 2) *reinterpret_cast<uint32_t*>(a.x_idx + ob / 4) = pw[0];
-      else *reinterpret_cast<u32x4*>(a.x_idx + ob) = u32x4{pw[0], pw[1 % NW], pw[2 % NW], pw[3 % NW]};
+      pw.store(a.x_idx + ob * BITS / 8);
       if (a.x_rot) {
         f32x4* xr = reinterpret_cast<f32x4*>(a.x_rot + ob);
 #pragma unroll
@@ -784,17 +817,21 @@ __global__ void __launch_bounds__(256) wq_kernel(const WqArgs a) {
   for (int w = 0; w < nt / 64; ++w) ss += red[w];
   const double n = sqrt(ss);
   const double den = n + OQ_EPS;
-  constexpr int PER = 8 / BITS;
-  for (int q = tid; q < d / PER; q += nt) {
-    uint32_t byte = 0;
-    for (int k = 0; k < PER; ++k) {
-      const double u = buf[q * PER + k] / den;
+  // groups of 8 indices = BITS bytes of the row's little-endian bit stream
+  // (d * BITS is a whole number of bytes, so a last short group ends on a byte)
+  const size_t row_bytes = (size_t)d * BITS / 8;
+  for (int q = tid; q < (d + 7) / 8; q += nt) {
+    uint64_t v = 0;
+    const int cnt = min(8, d - 8 * q);
+    for (int k = 0; k < cnt; ++k) {
+      const double u = buf[8 * q + k] / den;
       int lo = 0;
       for (int step = 128; step >= 1; step >>= 1)
         if (lo + step <= a.nthr && thr[lo + step - 1] < u) lo += step;
-      byte |= (uint32_t)lo << (k * BITS);
+      v |= (uint64_t)lo << (k * BITS);
     }
-    a.w_idx[o * (d / PER) + q] = (uint8_t)byte;
+    uint8_t* dst = a.w_idx + o * row_bytes + (size_t)q * BITS;
+    for (int b = 0; b < cnt * BITS / 8; ++b) dst[b] = (uint8_t)(v >> (8 * b));
   }
   if (tid == 0) a.w_norm[o] = (float)n;
 }
@@ -838,7 +875,9 @@ template <int LOG2H, bool BF16>
 hipError_t rq_dispatch_bits(const RqArgs& a, int bits, const RqPlan& p, hipStream_t st) {
   switch (bits) {
     case 2: return rq_go<LOG2H, BF16, 2>(a, p, st);
+    case 3: return rq_go<LOG2H, BF16, 3>(a, p, st);
     case 4: return rq_go<LOG2H, BF16, 4>(a, p, st);
+    case 6: return rq_go<LOG2H, BF16, 6>(a, p, st);
     case 8: return rq_go<LOG2H, BF16, 8>(a, p, st);
     default: return hipErrorInvalidValue;
   }
@@ -906,7 +945,9 @@ hipError_t rqw_dispatch(const RqArgs& a, int bits, const RqPlan& p, hipStream_t 
     constexpr int LG = decltype(lg)::value;
     switch (bits) {
       case 2: return rqw_dispatch_j<LG, BF16, 2>(a, p, st);
+      case 3: return rqw_dispatch_j<LG, BF16, 3>(a, p, st);
       case 4: return rqw_dispatch_j<LG, BF16, 4>(a, p, st);
+      case 6: return rqw_dispatch_j<LG, BF16, 6>(a, p, st);
       case 8: return rqw_dispatch_j<LG, BF16, 8>(a, p, st);
       default: return hipErrorInvalidValue;
     }
@@ -970,13 +1011,17 @@ hipError_t wq_launch(const WqArgs& a, bool bf16, int bits, hipStream_t st) {
   if (bf16) {
     switch (bits) {
       case 2: return wq_go<true, 2>(a, lds, st);
+      case 3: return wq_go<true, 3>(a, lds, st);
       case 4: return wq_go<true, 4>(a, lds, st);
+      case 6: return wq_go<true, 6>(a, lds, st);
       case 8: return wq_go<true, 8>(a, lds, st);
     }
   } else {
     switch (bits) {
       case 2: return wq_go<false, 2>(a, lds, st);
+      case 3: return wq_go<false, 3>(a, lds, st);
       case 4: return wq_go<false, 4>(a, lds, st);
+      case 6: return wq_go<false, 6>(a, lds, st);
       case 8: return wq_go<false, 8>(a, lds, st);
     }
   }

@@ -108,7 +108,7 @@ def test_block_rht_tables_through_both_kernels():
 @pytest.mark.parametrize("d,h,dtype", [(256, 2, "f32"), (256, 4, "bf16"), (256, 16, "f32"), (512, 32, "bf16"),
                                        (1024, 64, "f32"), (1024, 128, "bf16"), (2048, 256, "bf16"),
                                        (64, 64, "f32"), (16, 16, "bf16"), (12288, 256, "f32")])
-@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("bits", [2, 3, 4, 6, 8])
 def test_rotate_quantize_shapes_and_widths(d, h, dtype, bits):
     rng = np.random.default_rng(d * 7 + h + bits)
     T = 37
@@ -117,6 +117,15 @@ def test_rotate_quantize_shapes_and_widths(d, h, dtype, bits):
         x = synth.bf16_round(x)
     _, _, rep = P.check_activations(x, dtype, h, bits, name=f"shape d={d} h={h}")
     _assert_act(rep)
+
+
+@pytest.mark.parametrize("bits", [3, 6])
+@pytest.mark.parametrize("d_out,d,h", [(40, 3072, 256), (17, 1024, 64), (9, 256, 16)])
+def test_weight_quantization_non_byte_widths(bits, d_out, d, h):
+    rng = np.random.default_rng(bits * 100 + d)
+    Wm = rng.standard_normal((d_out, d)).astype(np.float32) / np.float32(np.sqrt(d))
+    _, _, rep = P.check_weights(Wm, h, bits, name=f"w{bits} d={d}")
+    _assert_w(rep)
 
 
 def test_zero_rows_single_token_and_repeatability():

@@ -95,7 +95,7 @@ def test_device_calls_reject_bad_arguments_without_launching():
     assert rq(h=48) == oq.OQ_EINVAL
     assert rq(h=512) == oq.OQ_EINVAL            # h does not divide d
     assert rq(d=250) == oq.OQ_EINVAL
-    assert rq(bits=3) == oq.OQ_EINVAL
+    assert rq(bits=5) == oq.OQ_EINVAL
     assert rq(T=-1) == oq.OQ_EINVAL
     assert rq(dt=7) == oq.OQ_EINVAL
     assert rq(x=None) == oq.OQ_EINVAL
@@ -106,7 +106,7 @@ def test_device_calls_reject_bad_arguments_without_launching():
     assert rq(idx=_fake((1 << 20) + 8)) == oq.OQ_EINVAL
     assert rq(T=0) == oq.OQ_OK                       # valid no-op
     # weights
-    assert L.oq_quantize_weights(f, oq.OQ_F32, 4, 256, 64, f, f, thp, 3, f, f, None) == oq.OQ_EINVAL
+    assert L.oq_quantize_weights(f, oq.OQ_F32, 4, 256, 64, f, f, thp, 5, f, f, None) == oq.OQ_EINVAL
     assert L.oq_quantize_weights(f, oq.OQ_F32, -1, 256, 64, f, f, thp, 4, f, f, None) == oq.OQ_EINVAL
     assert L.oq_quantize_weights(None, oq.OQ_F32, 4, 256, 64, f, f, thp, 4, f, f, None) == oq.OQ_EINVAL
     assert L.oq_quantize_weights(f, oq.OQ_F32, 0, 256, 64, f, f, thp, 4, f, f, None) == oq.OQ_OK
@@ -114,7 +114,7 @@ def test_device_calls_reject_bad_arguments_without_launching():
     c, _, _ = oq.oq_lloyd_max(256, 4)
     c2, _, _ = oq.oq_lloyd_max(256, 2)
     cp, c2p = c.ctypes.data, c2.ctypes.data
-    assert L.oq_qlinear(f, f, 4, f, f, 8, 256, cp, 4, cp, 3, None, 0, f, None) == oq.OQ_EINVAL
+    assert L.oq_qlinear(f, f, 4, f, f, 8, 256, cp, 4, cp, 5, None, 0, f, None) == oq.OQ_EINVAL
     assert L.oq_qlinear(f, f, 4, f, f, 8, 256, cp, 4, cp, 4, None, 5, f, None) == oq.OQ_EINVAL
     assert L.oq_qlinear(f, f, 4, f, f, 8, 256, None, 4, cp, 4, None, 0, f, None) == oq.OQ_EINVAL
     assert L.oq_qlinear(None, f, 4, f, f, 8, 256, cp, 4, cp, 4, None, 0, f, None) == oq.OQ_EINVAL
