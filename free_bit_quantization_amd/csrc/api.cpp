@@ -189,10 +189,12 @@ oq_status oq_qlinear(const uint8_t* x_idx, const float* s, int64_t T, const uint
   auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; };
   if (misaligned(x_idx) || misaligned(w_idx) || misaligned(w_norm) || misaligned(y) || misaligned(bias))
     return fail(OQ_EINVAL, "x_idx, w_idx, w_norm, bias and y must be 16-byte aligned");
-  const int kstage = bits_a == 8 ? 64 : 128;  // K indices per pipeline stage of the GEMM
+  const bool has_kernel = (bits_a == 4 && (bits_w == 2 || bits_w == 3 || bits_w == 4)) ||
+                          (bits_a == 8 && (bits_w == 2 || bits_w == 4)) || (bits_a == 3 && bits_w == 2) ||
+                          (bits_a == 6 && bits_w == 6);
+  if (!has_kernel) return fail(OQ_EUNSUPPORTED, "no GEMM kernel for W%dA%d", bits_w, bits_a);
+  const int kstage = (bits_a == 8 || bits_a == 6) ? 64 : 128;  // K indices per pipeline stage of the GEMM
   if (d_in % kstage != 0) return fail(OQ_EUNSUPPORTED, "d_in must be a multiple of %d for A%d (got %d)", kstage, bits_a, d_in);
-  if (!((bits_a == 4 || bits_a == 8) && (bits_w == 2 || bits_w == 4)))
-    return fail(OQ_EUNSUPPORTED, "no GEMM kernel for W%dA%d", bits_w, bits_a);
   const double sk = std::sqrt((double)d_in);
   for (int i = 0; i < La; ++i)
     if (std::fabs(sk * centroids_a[i]) > 60000.0) return fail(OQ_EINVAL, "sqrt(d_in)*centroids_a exceeds fp16");

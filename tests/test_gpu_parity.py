@@ -163,6 +163,16 @@ def test_gemm_gelu_epilogue_w2a4():
     run_linear(lin, bias=True)
 
 
+@pytest.mark.parametrize("bits_w,bits_a,T,d,d_out,h", [(3, 4, 300, 1024, 520, 256), (2, 3, 130, 3072, 300, 256),
+                                                      (6, 6, 200, 1024, 272, 64), (3, 4, 17, 256, 9, 16),
+                                                      (6, 6, 1, 64, 3, 64)])
+def test_gemm_non_byte_index_widths(bits_w, bits_a, T, d, d_out, h):
+    # 3- and 6-bit indices (W3A4, W2A3, W6A6): expanded to 4/8 bits while staged
+    lin = synth.Linear(f"w{bits_w}a{bits_a}", T, d, d_out, h, bits_w, bits_a, "student_t", "bf16", 10, 30.0, 0.5,
+                       5, 10.0)
+    run_linear(lin, bias=True, seed=bits_w * 10 + bits_a)
+
+
 def test_gemm_repeatable():
     lin = W["single_w4a4_64x256x256"].linears[0]
     x, Wm = synth.gen_linear(lin, 0, 0)
