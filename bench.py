@@ -34,8 +34,8 @@ FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, TFLOP/s
 # bench (FETCH_SIZE x 2, WRITE_SIZE x 1: the copy-kernel calibration), valid only
 # for the kernel source they were taken on (sha256 prefix); otherwise null.
 MEASURED_TRAFFIC = {
-    "free_bit_quantization_amd/csrc/qlinear.hip": ("f3cab77c4b727af7", 125.7e6, 169.9e6),
-    "free_bit_quantization_amd/csrc/rotate_quantize.hip": ("a7c5edf9fe070703", 28.8e6, 7.2e6),
+    "free_bit_quantization_amd/csrc/qlinear.hip": ("9ae076693d65c2db", 125.7e6, 169.9e6),
+    "free_bit_quantization_amd/csrc/rotate_quantize.hip": ("515e6c20d27cdd27", 28.8e6, 7.2e6),
 }
 
 
@@ -162,6 +162,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="one line per linear of every workload (tokens/s, GB/s, TFLOP/s, roofline fractions)")
+    ap.add_argument("--sweep-workloads", default="",
+                    help="comma-separated workload names for --sweep (default: all)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (the layer is "
@@ -176,7 +178,8 @@ def main():
     dev = torch.device("cuda:0")
 
     if args.sweep:
-        for name in synth.WORKLOAD_ORDER:
+        names = [n for n in args.sweep_workloads.split(",") if n] or synth.WORKLOAD_ORDER
+        for name in names:
             for k, lin in enumerate(synth.workloads()[name].linears):
                 r = measure_linear(lin, k, args.steps, args.warmup, args.ring_mb, dev)
                 print(json.dumps({

@@ -62,7 +62,7 @@ def _lin(name, T, k, n, h, bw, ba, act="student_t", dtype="bf16", ao=None, aos=3
 
 
 def workloads() -> dict:
-    """The five workloads, by name."""
+    """The workloads, by name."""
     w = {}
     w["single_w4a4_64x256x256"] = Workload(
         "single_w4a4_64x256x256",
@@ -92,11 +92,17 @@ def workloads() -> dict:
         "flux_block_w4a8_b2", lins,
         note="all quantized linears of one FLUX.1-like double-stream block, batch 2 "
              "(cond + uncond concatenated along tokens); independent inputs per linear")
+    w["flux_qkv_other_widths"] = Workload(
+        "flux_qkv_other_widths",
+        [_lin("qkv_w3a4", 4608, 3072, 9216, 256, 3, 4),
+         _lin("qkv_w2a3", 4608, 3072, 9216, 256, 2, 3),
+         _lin("qkv_w6a6", 4608, 3072, 9216, 256, 6, 6)],
+        note="the FLUX.1-like QKV linear at the other index widths the pages name (W3A4, W2A3, W6A6)")
     return w
 
 
 WORKLOAD_ORDER = ["single_w4a4_64x256x256", "flux_qkv_w4a4", "flux_mlp_w2a4",
-                  "wan_ffn_w4a4", "flux_block_w4a8_b2"]
+                  "wan_ffn_w4a4", "flux_block_w4a8_b2", "flux_qkv_other_widths"]
 
 
 def bf16_round(x: np.ndarray) -> np.ndarray:
