@@ -30,8 +30,10 @@
  *   - Device calls are asynchronous and stream-ordered: OQ_OK means enqueued
  *     on `stream` (0 = the null stream).  T = 0 is a valid no-op.
  *   - Index order: index 0 is the most negative centroid.  Packed indices are
- *     row-major, contiguous along d_in, least-significant bits first within
- *     each byte: 2-bit = 4 per byte, 4-bit = 2 per byte, 8-bit = 1 per byte.
+ *     row-major, contiguous along d_in; index k of a row occupies bits
+ *     [k b, (k+1) b) of the row read as a little-endian bit stream.  For
+ *     b = 2, 4, 8 that is least-significant bits first within each byte (4, 2,
+ *     1 per byte); 3- and 6-bit indices straddle byte boundaries.
  *   - The only global state is the thread-local error message.
  */
 #ifndef OQ_H_
@@ -127,7 +129,7 @@ oq_status oq_lloyd_max(int32_t d, int32_t bits, double* centroids, double* thres
  * h          : RPBH block size (power of two, 2 .. 256).
  * perm, sign : dev [d_in] int32 / int8 from oq_build_rpbh(d_in, h, seed).
  * thresholds : host [2^bits_w - 1] double, strictly increasing.
- * bits_w     : 2, 4 or 8.
+ * bits_w     : 2, 3, 4, 6 or 8.
  * w_idx      : dev [d_out][d_in * bits_w / 8] bytes, written.
  * w_norm     : dev [d_out] float, written (n_o rounded to fp32).
  * Errors     : OQ_EINVAL, OQ_EUNSUPPORTED (h > 256), OQ_EDEVICE.
@@ -153,7 +155,7 @@ oq_status oq_quantize_weights(const void* W, oq_dtype w_dtype, int32_t d_out, in
  * h          : RPBH block size (power of two, 2 .. 256).
  * perm, sign : dev [d] int32 / int8 from oq_build_rpbh(d, h, seed).
  * thresholds : host [2^bits_a - 1] double, strictly increasing; used as fp32.
- * bits_a     : 2, 4 or 8.
+ * bits_a     : 2, 3, 4, 6 or 8.
  * x_idx      : dev [T][d * bits_a / 8] bytes, written.
  * s          : dev [T] float, written (the norm, without eps).
  * x_rot      : dev [T][d] float or NULL: the fp32 rotated rows (checking only).
@@ -179,12 +181,15 @@ oq_status oq_rotate_quantize_act(const void* x, oq_dtype x_dtype, int64_t T, int
  *
  * x_idx       : dev [T][d_in * bits_a / 8], from oq_rotate_quantize_act.
  * s           : dev [T] float.
- * T           : tokens >= 0.   d_out >= 0.   d_in: multiple of 128 (bits_a = 4)
- *               or of 64 (bits_a = 8).
+ * T           : tokens >= 0.   d_out >= 0.   d_in: multiple of 128 (bits_a = 3
+ *               or 4) or of 64 (bits_a = 6 or 8).
  * w_idx       : dev [d_out][d_in * bits_w / 8], from oq_quantize_weights.
  * w_norm      : dev [d_out] float.
- * centroids_a : host [2^bits_a] double, ascending.  bits_a: 4 or 8.
- * centroids_w : host [2^bits_w] double, ascending.  bits_w: 2 or 4.
+ * centroids_a : host [2^bits_a] double, ascending.
+ * centroids_w : host [2^bits_w] double, ascending.
+ *               (bits_w, bits_a) with a kernel: W4A4, W2A4, W4A8, W2A8 and the
+ *               other widths the pages name, W3A4, W2A3, W6A6.  3- and 6-bit
+ *               indices are widened to 4 and 8 bits as they are staged.
  * bias        : dev [d_out] float or NULL.
  * epilogue    : OQ_EPI_NONE or OQ_EPI_GELU_ERF.
  * y           : dev [T][d_out] float, written.

@@ -21,6 +21,8 @@ Modules:
 * :mod:`oracle.codebook`  -- the marginal f_d and the Lloyd-Max quantizer.
 * :mod:`oracle.quant`     -- weight / activation quantization, index
   packing, dequantized product, GELU.
+* :mod:`oracle.rtn`       -- INT4 round-to-nearest weights and the W4A16
+  linear of the AdaLN modulation projections.
 
 Every function computes in float64 and follows the pages' steps in their
 order; a library primitive (matmul, searchsorted, betainc) serves as a
