@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "liboq.so")
-SOURCES = ["api.cpp", "host_rpbh.cpp", "host_lloyd_max.cpp", "rotate_quantize.hip", "qlinear.hip"]
+SOURCES = ["api.cpp", "host_rpbh.cpp", "host_lloyd_max.cpp", "rotate_quantize.hip", "qlinear.hip", "w4a16.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -213,4 +213,38 @@ oq_status oq_qlinear(const uint8_t* x_idx, const float* s, int64_t T, const uint
   return ok();
 }
 
+oq_status oq_quantize_weights_int4(const void* W, oq_dtype w_dtype, int32_t d_out, int32_t d_in, int32_t group,
+                                   uint8_t* q, float* scale, hipStream_t stream) {
+  if (w_dtype != OQ_F32 && w_dtype != OQ_BF16) return fail(OQ_EINVAL, "w_dtype must be OQ_F32 or OQ_BF16");
+  if (d_out < 0 || d_in <= 0) return fail(OQ_EINVAL, "need d_out >= 0 and d_in > 0");
+  if (group <= 0 || group % 128 != 0 || d_in % group != 0)
+    return fail(OQ_EINVAL, "group must be a positive multiple of 128 dividing d_in (got %d, d_in %d)", group, d_in);
+  if (d_out > 0 && (!W || !q || !scale)) return fail(OQ_EINVAL, "NULL device pointer");
+  if (d_out == 0) return ok();
+  oq::RtnArgs a{W, d_out, d_in, group, q, scale};
+  hipError_t e = oq::rtn_launch(a, w_dtype == OQ_BF16, stream);
+  if (e != hipSuccess) return device_error(e, "oq_quantize_weights_int4 launch");
+  return ok();
+}
+
+oq_status oq_linear_w4a16(const void* x, oq_dtype x_dtype, int64_t T, const uint8_t* q, const float* scale,
+                          int32_t d_out, int32_t d_in, int32_t group, const float* bias, float* y,
+                          hipStream_t stream) {
+  if (x_dtype != OQ_BF16 && x_dtype != OQ_F16) return fail(OQ_EINVAL, "x_dtype must be OQ_BF16 or OQ_F16");
+  if (T < 0 || d_out < 0 || d_in <= 0) return fail(OQ_EINVAL, "need T >= 0, d_out >= 0, d_in > 0");
+  if (d_in % 128 != 0) return fail(OQ_EINVAL, "d_in must be a multiple of 128 (got %d)", d_in);
+  if (group <= 0 || group % 128 != 0 || d_in % group != 0)
+    return fail(OQ_EINVAL, "group must be a positive multiple of 128 dividing d_in (got %d, d_in %d)", group, d_in);
+  if (T > 0 && d_out > 0 && (!x || !q || !scale || !y)) return fail(OQ_EINVAL, "NULL device pointer");
+  auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; };
+  if (misaligned(x) || misaligned(q)) return fail(OQ_EINVAL, "x and q must be 16-byte aligned");
+  if (misaligned(scale) || misaligned(bias) || misaligned(y)) return fail(OQ_EINVAL, "scale, bias and y must be 16-byte aligned");
+  if ((T + 15) / 16 > 65535) return fail(OQ_EUNSUPPORTED, "T above %d has no launch shape", 65535 * 16);
+  if (T == 0 || d_out == 0) return ok();
+  oq::W4Args a{x, T, d_in, d_out, q, scale, group, bias, y};
+  hipError_t e = oq::w4a_launch(a, x_dtype == OQ_BF16, stream);
+  if (e != hipSuccess) return device_error(e, "oq_linear_w4a16 launch");
+  return ok();
+}
+
 }  // extern "C"

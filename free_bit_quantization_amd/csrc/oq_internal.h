@@ -85,6 +85,30 @@ struct QlArgs {
 };
 hipError_t ql_launch(const QlArgs& a, int bits_a, int bits_w, hipStream_t stream);
 
+// ---- INT4 round-to-nearest weight-only linear (AdaLN modulation) --------------
+struct RtnArgs {
+  const void* W;      // [N][K] fp32 or bf16
+  int32_t N;
+  int32_t K;
+  int32_t group;      // input columns per scale, multiple of 128 dividing K
+  uint8_t* q;         // [N][K / 2] two's-complement nibbles
+  float* scale;       // [N][K / group]
+};
+hipError_t rtn_launch(const RtnArgs& a, bool bf16, hipStream_t stream);
+
+struct W4Args {
+  const void* x;      // [T][K] bf16 or fp16
+  int64_t T;
+  int32_t K;
+  int32_t N;
+  const uint8_t* q;
+  const float* scale;
+  int32_t group;
+  const float* bias;  // [N] or null
+  float* y;           // [T][N]
+};
+hipError_t w4a_launch(const W4Args& a, bool bf16, hipStream_t stream);
+
 }  // namespace oq
 
 #endif  // OQ_INTERNAL_H_

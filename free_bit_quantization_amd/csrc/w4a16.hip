@@ -1,0 +1,210 @@
+// INT4 round-to-nearest weight-only linear (W4A16) for the AdaLN modulation
+// projections, which stay outside the OrbitQuant codebooks: their
+// timestep-dependent scale and shift cannot absorb the rotation, and the
+// method keeps them at INT4 weight round-to-nearest ("OrbitQuant:
+// data-agnostic quantization for image and video", rcap.io summary:
+// deployment paragraph and AdaLN caveat; FLUX.2 Klein OrbitQuant W4A8 model
+// card, Components table).
+//
+// Scheme: symmetric signed codes q in [-8, 7]; one fp32 scale
+// s = max|w| / 7 per output row and group of `group` input columns;
+// q = clamp(rint(w / s), -8, 7) with the stored fp32 s (fp64 division);
+// codes packed as two's-complement nibbles, code k in bits [4k, 4k + 4) of
+// the row.  y[t][o] = sum_g s[o][g] sum_{k in g} q[o][k] x[t][k] (+ bias[o]).
+//
+// rtn_kernel  : the offline quantizer, one wavefront per (row, group), fp64.
+// w4a_kernel  : the product.  The modulation input is one row per image of
+//   the batch, so T is tiny and the kernel streams the packed weights once
+//   from HBM (0.5 byte per weight): bound by HBM bandwidth.  A workgroup owns
+//   16 output features and 16 tokens; its 8 wavefronts split d_in.  Codes are
+//   decoded through a 256-entry LDS table (one byte = two codes -> two 16-bit
+//   values) into the B operand of v_mfma_f32_16x16x32_{bf16,f16} (codes are
+//   exact in both types), activations are the A operand as loaded, fp32
+//   accumulation; each group's sum is scaled into a running total, and the 8
+//   partial tiles are summed through LDS in a fixed order.
+
+#include "oq_internal.h"
+
+namespace oq {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWaves = 8;          // split of d_in inside a workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTile = 16;          // tokens x features per workgroup
+constexpr int kBatch = 2;          // 128-wide K chunks loaded per batch
+constexpr int kRedStride = 17;     // padded row of the reduction buffer
+
+// ---- offline quantizer ---------------------------------------------------------
+template <bool BF16>
+__global__ void __launch_bounds__(256) rtn_kernel(const RtnArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int ng = a.K / a.group;
+  if (wid >= (int64_t)a.N * ng) return;   // whole wavefronts exit together
+  const int64_t row = wid / ng;
+  const int g = (int)(wid % ng);
+  const int64_t base = row * a.K + (int64_t)g * a.group;
+  auto ld = [&](int64_t i) -> double {
+    if (BF16) return (double)__uint_as_float((uint32_t)static_cast<const uint16_t*>(a.W)[i] << 16);
+    return (double)static_cast<const float*>(a.W)[i];
+  };
+  double m = 0.0;
+  for (int k = lane; k < a.group; k += 64) m = fmax(m, fabs(ld(base + k)));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmax(m, __shfl_xor(m, o));
+  const float s = (float)(m / 7.0);
+  const double sd = (double)s;
+  // lane handles bytes (code pairs) lane, lane + 64, ...
+  for (int b = lane; b < a.group / 2; b += 64) {
+    uint32_t nib[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      int q = 0;
+      if (sd > 0.0) q = (int)fmin(fmax(rint(ld(base + 2 * b + e) / sd), -8.0), 7.0);
+      nib[e] = (uint32_t)q & 15u;
+    }
+    a.q[(base >> 1) + b] = (uint8_t)(nib[0] | (nib[1] << 4));
+  }
+  if (lane == 0) a.scale[row * ng + g] = s;
+}
+
+// ---- the product -------------------------------------------------------------------
+template <bool BF16>
+__device__ __forceinline__ f32x4 mfma(const u32x4 a, const u32x4 b, const f32x4 c) {
+  if constexpr (BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a), __builtin_bit_cast(half8, b), c, 0,
+                                                  0, 0);
+}
+
+// The 8 codes of word w (code j in bits [4j, 4j+4)) as 8 16-bit values: one
+// table entry per byte holds the values of its low and high nibble.
+__device__ __forceinline__ u32x4 decode8(const uint32_t* tab, uint32_t w) {
+  return u32x4{tab[w & 0xFFu], tab[(w >> 8) & 0xFFu], tab[(w >> 16) & 0xFFu], tab[w >> 24]};
+}
+
+// v_mfma_f32_16x16x32: lane l holds A[l % 16][8 (l / 16) .. +8], B[8 (l / 16) .. +8][l % 16]
+// and D[4 (l / 16) .. +4][l % 16].  A = activations (rows = tokens), B = decoded
+// codes (columns = output features).  Lane (l % 16, j = l / 16) loads the 16
+// bytes (32 codes) k = 128 c + 32 j + [0, 32) of its feature for 128-wide chunk
+// c; MFMA step s takes codes 8 s .. 8 s + 7 of them and the activations of the
+// same 8 k, so each step sums a permutation of 32 columns of chunk c.
+template <bool BF16>
+__global__ void __launch_bounds__(kThreads) w4a_kernel(const W4Args a) {
+  __shared__ __align__(16) uint32_t tab[256];
+  __shared__ __align__(16) float red[kWaves * kTile * kRedStride];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 15, j = lane >> 4;
+  const int n0 = blockIdx.x * kTile;
+  const int64_t t0 = (int64_t)blockIdx.y * kTile;
+  const int K = a.K, N = a.N;
+  const int64_t T = a.T;
+
+  if (tid < 256) {
+    // byte e = (hi nibble, lo nibble) of two's-complement codes -> two exact 16-bit values
+    const int lo = (tid & 15) - ((tid & 8) << 1), hi = (tid >> 4) - ((tid & 128) >> 3);
+    uint32_t vlo, vhi;
+    if (BF16) {
+      vlo = __float_as_uint((float)lo) >> 16;   // small integers: the top 16 bits are exact
+      vhi = __float_as_uint((float)hi) >> 16;
+    } else {
+      vlo = __builtin_bit_cast(uint16_t, (_Float16)lo);
+      vhi = __builtin_bit_cast(uint16_t, (_Float16)hi);
+    }
+    tab[tid] = vlo | (vhi << 16);
+  }
+
+  const int n = n0 + lr < N ? n0 + lr : N - 1;
+  const int64_t t = t0 + lr;
+  const bool trow = t < T;
+  const uint8_t* qrow = a.q + (size_t)n * (K / 2) + j * 16;
+  const uint16_t* xrow = static_cast<const uint16_t*>(a.x) + (size_t)(trow ? t : 0) * K + j * 32;
+  const float* srow = a.scale + (size_t)n * (K / a.group);
+
+  // this wavefront's 128-wide chunks
+  const int C = K / 128;
+  const int c0 = (int)((int64_t)C * wave / kWaves), c1 = (int)((int64_t)C * (wave + 1) / kWaves);
+  const int cpg = a.group / 128;   // chunks per group
+
+  __syncthreads();   // table ready
+
+  f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f}, acc = tot;
+  for (int cb = c0; cb < c1; cb += kBatch) {
+    u32x4 wq[kBatch], xa[kBatch][4];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int c = cb + i < c1 ? cb + i : c1 - 1;
+      wq[i] = *reinterpret_cast<const u32x4*>(qrow + (size_t)c * 64);
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        xa[i][st] = trow ? *reinterpret_cast<const u32x4*>(xrow + (size_t)c * 128 + 8 * st) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int c = cb + i;
+      if (c < c1) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st) acc = mfma<BF16>(xa[i][st], decode8(tab, wq[i][st]), acc);
+        // end of a group (or of this wavefront's range): scale it into the total
+        if ((c + 1) % cpg == 0 || c + 1 == c1) {
+          const float sc = srow[c / cpg];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) tot[r] = fmaf(sc, acc[r], tot[r]);
+          acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    }
+  }
+
+  // partial tiles -> LDS, then a fixed-order sum over the wavefronts
+  const int rows = T - t0 < kTile ? (int)(T - t0) : kTile;
+  float* rw = red + wave * kTile * kRedStride;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = 4 * j + r;
+    if (row < rows) rw[row * kRedStride + lr] = tot[r];
+  }
+  __syncthreads();
+  for (int e = tid; e < rows * kTile; e += kThreads) {
+    const int row = e / kTile, col = e % kTile;
+    if (n0 + col >= N) continue;
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) v += red[(w * kTile + row) * kRedStride + col];
+    if (a.bias) v += a.bias[n0 + col];
+    a.y[(size_t)(t0 + row) * N + n0 + col] = v;
+  }
+}
+
+}  // namespace
+
+hipError_t rtn_launch(const RtnArgs& a, bool bf16, hipStream_t st) {
+  const int64_t waves = (int64_t)a.N * (a.K / a.group);
+  if (waves == 0) return hipSuccess;
+  const int64_t grid = (waves + 3) / 4;
+  if (grid > 0x7FFFFFFF) return hipErrorInvalidValue;
+  if (bf16) hipLaunchKernelGGL(rtn_kernel<true>, dim3((unsigned)grid), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(rtn_kernel<false>, dim3((unsigned)grid), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t w4a_launch(const W4Args& a, bool bf16, hipStream_t st) {
+  if (a.T == 0 || a.N == 0) return hipSuccess;
+  const int64_t gy = (a.T + kTile - 1) / kTile;   // token tiles
+  if (gy > 65535) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((a.N + kTile - 1) / kTile), (unsigned)gy);
+  if (bf16) hipLaunchKernelGGL(w4a_kernel<true>, grid, dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL(w4a_kernel<false>, grid, dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace oq

@@ -19,12 +19,13 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "liboq.so")
 
 OQ_OK, OQ_EINVAL, OQ_EUNSUPPORTED, OQ_ENOCONV, OQ_EDEVICE = 0, -1, -2, -3, -4
-OQ_F32, OQ_BF16 = 0, 1
+OQ_F32, OQ_BF16, OQ_F16 = 0, 1, 2
 OQ_EPI_NONE, OQ_EPI_GELU_ERF = 0, 1
 
 # every symbol include/oq.h declares
 EXPORTS = ("oq_last_error", "oq_version", "oq_build_rpbh", "oq_build_block_rht", "oq_lloyd_max",
-           "oq_quantize_weights", "oq_rotate_quantize_act", "oq_qlinear")
+           "oq_quantize_weights", "oq_rotate_quantize_act", "oq_qlinear", "oq_quantize_weights_int4",
+           "oq_linear_w4a16")
 
 
 class OQError(RuntimeError):
@@ -64,6 +65,10 @@ def lib() -> ctypes.CDLL:
         L.oq_rotate_quantize_act.argtypes = [_P, _I32, _I64, _I32, _I32, _P, _P, _P, _I32, _P, _P, _P, _P]
         L.oq_qlinear.restype = _I32
         L.oq_qlinear.argtypes = [_P, _P, _I64, _P, _P, _I32, _I32, _P, _I32, _P, _I32, _P, _I32, _P, _P]
+        L.oq_quantize_weights_int4.restype = _I32
+        L.oq_quantize_weights_int4.argtypes = [_P, _I32, _I32, _I32, _I32, _P, _P, _P]
+        L.oq_linear_w4a16.restype = _I32
+        L.oq_linear_w4a16.argtypes = [_P, _I32, _I64, _P, _P, _I32, _I32, _I32, _P, _P, _P]
         _lib = L
     return _lib
 
@@ -196,4 +201,37 @@ def oq_qlinear(x_idx, s, w_idx, w_norm, d_in: int, centroids_a, bits_a: int, cen
                             _dev(w_norm, torch.float32), d_out, d_in, cap, bits_a, cwp, bits_w,
                             _dev(bias, torch.float32) if bias is not None else None, epilogue,
                             _dev(y, torch.float32), _stream(stream)))
+    return y
+
+
+def oq_quantize_weights_int4(W, group: int, q=None, scale=None, stream=None):
+    """INT4 round-to-nearest weights (AdaLN modulation): returns
+    (q uint8[d_out, d_in/2], scale f32[d_out, d_in/group])."""
+    import torch
+    d_out, d_in = W.shape
+    if q is None:
+        q = torch.empty((d_out, d_in // 2), dtype=torch.uint8, device=W.device)
+    if scale is None:
+        scale = torch.empty((d_out, d_in // group), dtype=torch.float32, device=W.device)
+    _check(lib().oq_quantize_weights_int4(_dev(W), _dtype_code(W), d_out, d_in, group, _dev(q, torch.uint8),
+                                          _dev(scale, torch.float32), _stream(stream)))
+    return q, scale
+
+
+def oq_linear_w4a16(x, q, scale, group: int, bias=None, y=None, stream=None):
+    """W4A16 product with INT4 RTN weights: returns y f32[T, d_out]; x is bf16 or fp16."""
+    import torch
+    T, d_in = x.shape
+    d_out = q.shape[0]
+    if x.dtype == torch.bfloat16:
+        code = OQ_BF16
+    elif x.dtype == torch.float16:
+        code = OQ_F16
+    else:
+        raise TypeError("x must be bfloat16 or float16")
+    if y is None:
+        y = torch.empty((T, d_out), dtype=torch.float32, device=x.device)
+    _check(lib().oq_linear_w4a16(_dev(x), code, T, _dev(q, torch.uint8), _dev(scale, torch.float32), d_out, d_in,
+                                 group, _dev(bias, torch.float32) if bias is not None else None,
+                                 _dev(y, torch.float32), _stream(stream)))
     return y

@@ -150,3 +150,50 @@ def gen_linear(lin: Linear, seed: int = 0, index: int = 0, T: Optional[int] = No
 def gen_bias(n: int, seed: int = 0) -> np.ndarray:
     """A small seeded bias vector (tests of the bias epilogue)."""
     return (0.1 * np.random.default_rng(np.random.SeedSequence([seed, 999])).standard_normal(n)).astype(np.float32)
+
+
+# ---- AdaLN modulation projections (INT4 round-to-nearest weights, 16-bit input)
+
+
+@dataclasses.dataclass(frozen=True)
+class ModLinear:
+    """A modulation projection: the conditioning vector (one row per image of
+    the batch) -> shift / scale / gate of the block's norms."""
+    name: str
+    T: int                  # rows (images in the batch)
+    d_in: int
+    d_out: int
+    group: int              # input columns per INT4 scale (d_in = per output row)
+    act_dtype: str = "bf16"  # "bf16" | "f16"
+    w_outliers: int = 0
+    w_outlier_scale: float = 10.0
+
+
+def modulation_workloads() -> dict:
+    """FLUX.1-like double-stream block, batch 2: two modulation projections
+    of 3072 -> 6 x 3072 (image and text stream), per-row and per-128 scales."""
+    return {
+        "flux_adaln_mod_w4a16_b2": [ModLinear("img_mod", 2, 3072, 18432, 3072, w_outliers=15),
+                                    ModLinear("txt_mod_g128", 2, 3072, 18432, 128, w_outliers=15)],
+    }
+
+
+def gen_modulation(lin: ModLinear, seed: int = 0, T: Optional[int] = None):
+    """Draw (x[T, d_in] fp32 holding bf16 / fp16 values, W[d_out, d_in] fp32).
+
+    x is SiLU of a standard normal conditioning vector (the modulation input
+    is SiLU of the timestep + pooled-text embedding), rounded to the 16-bit
+    type; W is N(0, 1/d_in) with a few outlier input columns."""
+    T = lin.T if T is None else T
+    r_act, r_w, r_wcol = [np.random.default_rng(s) for s in np.random.SeedSequence([seed, 7001]).spawn(3)]
+    z = r_act.standard_normal((T, lin.d_in))
+    x = (z / (1.0 + np.exp(-z))).astype(np.float32)
+    if lin.act_dtype == "bf16":
+        x = bf16_round(x)
+    else:
+        x = x.astype(np.float16).astype(np.float32)
+    W = r_w.standard_normal((lin.d_out, lin.d_in), dtype=np.float32) * np.float32(1.0 / np.sqrt(lin.d_in))
+    if lin.w_outliers:
+        col = r_wcol.choice(lin.d_in, lin.w_outliers, replace=False)
+        W[:, col] *= np.float32(lin.w_outlier_scale)
+    return x, W

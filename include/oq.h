@@ -55,7 +55,7 @@ enum {
   OQ_EDEVICE = -4        /* HIP runtime or launch error */
 };
 
-typedef enum { OQ_F32 = 0, OQ_BF16 = 1 } oq_dtype;
+typedef enum { OQ_F32 = 0, OQ_BF16 = 1, OQ_F16 = 2 } oq_dtype;
 enum { OQ_EPI_NONE = 0, OQ_EPI_GELU_ERF = 1 };
 
 /* eps added to the activation norm (and to weight row norms) before the
@@ -201,6 +201,56 @@ oq_status oq_qlinear(const uint8_t* x_idx, const float* s, int64_t T,
                      const double* centroids_a, int32_t bits_a,
                      const double* centroids_w, int32_t bits_w,
                      const float* bias, int32_t epilogue, float* y, hipStream_t stream);
+
+/*
+ * oq_quantize_weights_int4 -- INT4 round-to-nearest, weight only, for the
+ * AdaLN modulation projections, which the method keeps out of the codebooks:
+ * their timestep-dependent scale and shift cannot absorb the rotation
+ * (rcap.io summary: deployment paragraph and AdaLN caveat; FLUX.2 Klein
+ * OrbitQuant W4A8 model card, Components table).  The pages name only "INT4
+ * weight round-to-nearest"; the scheme here is symmetric:
+ *
+ *   s[o][g] = fp32(max_{k in g} |W[o][k]| / 7)      (fp64 division)
+ *   q[o][k] = clamp(rint(W[o][k] / s[o][g]), -8, 7)  (fp64, half to even;
+ *                                                     q = 0 where s = 0)
+ *
+ * Offline, not on the hot path.
+ *
+ * W       : dev [d_out][d_in], fp32 or bf16 (w_dtype), row-major.
+ * d_out   : >= 0.   d_in: > 0.
+ * group   : input columns per scale: a multiple of 128 dividing d_in (d_in =
+ *           one scale per output row).
+ * q       : dev [d_out][d_in / 2] bytes, written: two's-complement nibbles,
+ *           code k in bits [4k, 4k + 4) of the row (low nibble first).
+ * scale   : dev [d_out][d_in / group] float, written.
+ * Errors  : OQ_EINVAL, OQ_EDEVICE.
+ */
+oq_status oq_quantize_weights_int4(const void* W, oq_dtype w_dtype, int32_t d_out, int32_t d_in, int32_t group,
+                                   uint8_t* q, float* scale, hipStream_t stream);
+
+/*
+ * oq_linear_w4a16 -- the AdaLN modulation projection with INT4 RTN weights
+ * and 16-bit activations (same passages as oq_quantize_weights_int4):
+ *
+ *   y[t][o] = sum_g s[o][g] sum_{k in g} q[o][k] x[t][k]   (+ bias[o])
+ *
+ * Codes are decoded through an LDS table into exact bf16 / fp16 MFMA
+ * operands; fp32 accumulation; each group's sum is scaled into an fp32
+ * total.  Built for the modulation shape (T = images in the batch, a few
+ * rows): it streams the packed weights once and is bound by HBM bandwidth.
+ *
+ * x       : dev [T][d_in], bf16 or fp16 (x_dtype), row-major.
+ * T       : >= 0 rows, at most 65535 * 16.
+ * q, scale: from oq_quantize_weights_int4 with the same d_out, d_in, group.
+ * d_in    : multiple of 128.   group: multiple of 128 dividing d_in.
+ * bias    : dev [d_out] float or NULL.
+ * y       : dev [T][d_out] float, written.
+ * x, q, scale, bias and y must be 16-byte aligned (OQ_EINVAL otherwise).
+ * Errors  : OQ_EINVAL, OQ_EUNSUPPORTED, OQ_EDEVICE.
+ */
+oq_status oq_linear_w4a16(const void* x, oq_dtype x_dtype, int64_t T, const uint8_t* q, const float* scale,
+                          int32_t d_out, int32_t d_in, int32_t group, const float* bias, float* y,
+                          hipStream_t stream);
 
 #ifdef __cplusplus
 }

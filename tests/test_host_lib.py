@@ -125,3 +125,30 @@ def test_device_calls_reject_bad_arguments_without_launching():
     assert L.oq_qlinear(g, f, 4, f, f, 8, 256, cp, 4, cp, 4, None, 0, f, None) == oq.OQ_EINVAL
     assert L.oq_qlinear(f, f, 4, f, f, 8, 256, cp, 4, cp, 4, g, 0, f, None) == oq.OQ_EINVAL   # bias
     assert L.oq_qlinear(f, f, 4, f, f, 8, 256, cp, 4, cp, 4, None, 0, g, None) == oq.OQ_EINVAL   # y
+
+
+def test_int4_rtn_entry_points_reject_invalid_arguments():
+    # only rejected calls and no-ops: nothing here may reach a launch
+    L = oq.lib()
+    f = _fake()
+    g = _fake((1 << 20) + 4)
+    q4 = L.oq_quantize_weights_int4
+    assert q4(f, oq.OQ_F16, 8, 256, 256, f, f, None) == oq.OQ_EINVAL        # weights: fp32 / bf16 only
+    assert q4(f, oq.OQ_F32, 8, 256, 64, f, f, None) == oq.OQ_EINVAL          # group not a multiple of 128
+    assert q4(f, oq.OQ_F32, 8, 384, 256, f, f, None) == oq.OQ_EINVAL         # group does not divide d_in
+    assert q4(f, oq.OQ_F32, -1, 256, 256, f, f, None) == oq.OQ_EINVAL
+    assert q4(None, oq.OQ_F32, 8, 256, 256, f, f, None) == oq.OQ_EINVAL
+    assert q4(f, oq.OQ_F32, 0, 256, 128, f, f, None) == oq.OQ_OK             # no rows: no-op
+    lw = L.oq_linear_w4a16
+    assert lw(f, oq.OQ_F32, 2, f, f, 64, 256, 256, None, f, None) == oq.OQ_EINVAL    # A16 only
+    assert lw(f, oq.OQ_BF16, 2, f, f, 64, 192, 192, None, f, None) == oq.OQ_EINVAL   # d_in % 128
+    assert lw(f, oq.OQ_BF16, 2, f, f, 64, 512, 192, None, f, None) == oq.OQ_EINVAL   # group
+    assert lw(f, oq.OQ_BF16, -1, f, f, 64, 256, 256, None, f, None) == oq.OQ_EINVAL
+    assert lw(None, oq.OQ_BF16, 2, f, f, 64, 256, 256, None, f, None) == oq.OQ_EINVAL
+    assert lw(g, oq.OQ_BF16, 2, f, f, 64, 256, 256, None, f, None) == oq.OQ_EINVAL   # x alignment
+    assert lw(f, oq.OQ_BF16, 2, g, f, 64, 256, 256, None, f, None) == oq.OQ_EINVAL   # q alignment
+    assert lw(f, oq.OQ_BF16, 2, f, f, 64, 256, 256, g, f, None) == oq.OQ_EINVAL     # bias alignment
+    assert lw(f, oq.OQ_F16, 65535 * 16 + 1, f, f, 64, 256, 256, None, f, None) == oq.OQ_EUNSUPPORTED
+    assert lw(f, oq.OQ_F16, 0, f, f, 64, 256, 256, None, f, None) == oq.OQ_OK       # T = 0: no-op
+    assert lw(f, oq.OQ_BF16, 4, f, f, 0, 256, 128, None, f, None) == oq.OQ_OK       # d_out = 0: no-op
+    assert oq.lib().oq_last_error() is not None
