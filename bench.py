@@ -12,7 +12,8 @@ the activation batches rotate through a ring of buffers larger than the
 Prints one JSON line.  Per-kernel durations come from HIP events recorded
 on the launch stream around every kernel of the timed steps.  With --sweep it
 prints one line per linear of every workload instead (throughput and roofline
-fractions only).
+fractions only); with --modulation one line per AdaLN modulation projection
+(the INT4 round-to-nearest W4A16 kernel, HBM roofline).
 """
 
 from __future__ import annotations
@@ -152,6 +153,60 @@ def measure_linear(lin, index, steps, warmup, ring_mb, dev):
     return r
 
 
+def measure_modulation(lin, steps, warmup, ring_mb, dev):
+    """Time the W4A16 modulation projection (INT4 RTN weights streamed from HBM).
+
+    The packed weights rotate through a ring of copies larger than the
+    Infinity Cache.  The kernel is a few microseconds long, shorter than a
+    host launch, so the stream is held by a spin kernel while every timed
+    launch is enqueued; one pair of HIP events then brackets the launches
+    running back to back on the GPU (per-launch events would add their own
+    overhead to a kernel this short)."""
+    import torch
+    from free_bit_quantization_amd import oq, synth
+
+    T, K, N, g = lin.T, lin.d_in, lin.d_out, lin.group
+    x, Wm = synth.gen_modulation(lin, seed=0)
+    xt = torch.from_numpy(x).to(dev)
+    xt = xt.to(torch.bfloat16) if lin.act_dtype == "bf16" else xt.to(torch.float16)
+    Wd = torch.from_numpy(Wm).to(dev)
+    q, sc = oq.oq_quantize_weights_int4(Wd, g)
+    del Wd
+    wbytes = q.numel() + sc.numel() * 4
+    nring = max(1, math.ceil(ring_mb * 1e6 / wbytes))
+    ring = [(q, sc)] + [(q.clone(), sc.clone()) for _ in range(1, nring)]
+    y = torch.empty((T, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        oq.oq_linear_w4a16(xt, ring[i % nring][0], ring[i % nring][1], g, y=y, stream=stream)
+    torch.cuda.synchronize()
+    reps = []
+    for _ in range(3):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(int(1.0e7 + 2.0e5 * steps))   # >= 5 ms + 100 us per launch
+        e0.record(stream)
+        for i in range(steps):
+            oq.oq_linear_w4a16(xt, ring[i % nring][0], ring[i % nring][1], g, y=y, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        reps.append(e0.elapsed_time(e1) / steps)
+    reps.sort()
+    t_avg = reps[1]   # median of three back-to-back runs
+    alg = N * K // 2 + N * (K // g) * 4 + T * K * xt.element_size() + T * N * 4
+    return dict(T=T, K=K, N=N, group=g, nring=nring, t_ms=t_avg, t_runs=reps,
+                bytes=alg, gbs=alg / (t_avg * 1e-3) / 1e9)
+
+
+def modulation_line(name, lin, r):
+    return {"workload": name, "linear": lin.name, "kernel": "oq_linear_w4a16 (w4a_kernel)",
+            "tokens": r["T"], "d_in": r["K"], "d_out": r["N"], "group": r["group"], "act_dtype": lin.act_dtype,
+            "ms": round(r["t_ms"], 5), "ms_runs": [round(t, 5) for t in r["t_runs"]],
+            "roofline": {"bound": "hbm", "achieved": round(r["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(r["gbs"] / HBM_PEAK_GBS, 4),
+                         "algorithmic": f"N*K/2 + N*(K/group)*4 + T*K*2 + T*N*4 = {r['bytes']} B"},
+            "weight_ring_buffers": r["nring"]}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -162,6 +217,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true",
                     help="one line per linear of every workload (tokens/s, GB/s, TFLOP/s, roofline fractions)")
+    ap.add_argument("--modulation", action="store_true",
+                    help="one line per AdaLN modulation projection (INT4 RTN W4A16 kernel)")
     ap.add_argument("--sweep-workloads", default="",
                     help="comma-separated workload names for --sweep (default: all)")
     args = ap.parse_args()
@@ -176,6 +233,13 @@ def main():
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
+
+    if args.modulation:
+        for name, lins in synth.modulation_workloads().items():
+            for lin in lins:
+                r = measure_modulation(lin, max(args.steps, 50), args.warmup, args.ring_mb, dev)
+                print(json.dumps(modulation_line(name, lin, r)), flush=True)
+        return
 
     if args.sweep:
         names = [n for n in args.sweep_workloads.split(",") if n] or synth.WORKLOAD_ORDER

@@ -1,6 +1,7 @@
 // C ABI of liboq: argument validation, launch planning, error reporting.
 // Every entry point validates all arguments before launching anything; an
 // invalid argument returns OQ_EINVAL with no side effect.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -239,9 +240,13 @@ oq_status oq_linear_w4a16(const void* x, oq_dtype x_dtype, int64_t T, const uint
   auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; };
   if (misaligned(x) || misaligned(q)) return fail(OQ_EINVAL, "x and q must be 16-byte aligned");
   if (misaligned(scale) || misaligned(bias) || misaligned(y)) return fail(OQ_EINVAL, "scale, bias and y must be 16-byte aligned");
-  if ((T + 15) / 16 > 65535) return fail(OQ_EUNSUPPORTED, "T above %d has no launch shape", 65535 * 16);
+  if (2 * (int64_t)d_in + 16 > 96 * 1024) return fail(OQ_EUNSUPPORTED, "d_in %d too large for the LDS row", d_in);
+  {
+    const int64_t tt = std::min<int64_t>(16, (96 * 1024) / (2 * (int64_t)d_in + 16));
+    if ((T + tt - 1) / tt > 65535) return fail(OQ_EUNSUPPORTED, "T %lld has no launch shape", (long long)T);
+  }
   if (T == 0 || d_out == 0) return ok();
-  oq::W4Args a{x, T, d_in, d_out, q, scale, group, bias, y};
+  oq::W4Args a{x, T, d_in, d_out, q, scale, group, bias, y, 0};
   hipError_t e = oq::w4a_launch(a, x_dtype == OQ_BF16, stream);
   if (e != hipSuccess) return device_error(e, "oq_linear_w4a16 launch");
   return ok();

@@ -106,6 +106,7 @@ struct W4Args {
   int32_t group;
   const float* bias;  // [N] or null
   float* y;           // [T][N]
+  int32_t tt;         // tokens per workgroup (set by w4a_launch)
 };
 hipError_t w4a_launch(const W4Args& a, bool bf16, hipStream_t stream);
 

@@ -16,7 +16,7 @@
 // w4a_kernel  : the product.  The modulation input is one row per image of
 //   the batch, so T is tiny and the kernel streams the packed weights once
 //   from HBM (0.5 byte per weight): bound by HBM bandwidth.  A workgroup owns
-//   16 output features and 16 tokens; its 8 wavefronts split d_in.  Codes are
+//   32 output features and up to 16 tokens; its 8 wavefronts split d_in.  Codes are
 //   decoded through a 256-entry LDS table (one byte = two codes -> two 16-bit
 //   values) into the B operand of v_mfma_f32_16x16x32_{bf16,f16} (codes are
 //   exact in both types), activations are the A operand as loaded, fp32
@@ -33,11 +33,14 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 
-constexpr int kWaves = 8;          // split of d_in inside a workgroup
+constexpr int kWaves = 8;            // split of d_in inside a workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kTile = 16;          // tokens x features per workgroup
-constexpr int kBatch = 2;          // 128-wide K chunks loaded per batch
-constexpr int kRedStride = 17;     // padded row of the reduction buffer
+constexpr int kFeat = 32;            // output features per workgroup (two MFMA tiles)
+constexpr int kBatch = 3;            // 128-wide K chunks whose weights are loaded at once
+constexpr int kRedStride = kFeat + 1;  // padded row of the reduction buffer
+constexpr int kTabBytes = 1024;
+constexpr int kRedBytes = kWaves * 16 * kRedStride * 4;
+constexpr int kXLdsMax = 96 * 1024;  // staged activation rows
 
 // ---- offline quantizer ---------------------------------------------------------
 template <bool BF16>
@@ -96,19 +99,77 @@ __device__ __forceinline__ u32x4 decode8(const uint32_t* tab, uint32_t w) {
 // bytes (32 codes) k = 128 c + 32 j + [0, 32) of its feature for 128-wide chunk
 // c; MFMA step s takes codes 8 s .. 8 s + 7 of them and the activations of the
 // same 8 k, so each step sums a permutation of 32 columns of chunk c.
+//
+// A workgroup owns kFeat = 32 features (two 16-wide B tiles sharing each A
+// fragment) and up to 16 tokens, whose rows are staged once in LDS (row stride
+// padded by 16 bytes so that the 16 rows of a fragment read fall in distinct
+// banks).  Each wavefront issues the weight loads of kBatch chunks at once.
 template <bool BF16>
-__global__ void __launch_bounds__(kThreads) w4a_kernel(const W4Args a) {
-  __shared__ __align__(16) uint32_t tab[256];
-  __shared__ __align__(16) float red[kWaves * kTile * kRedStride];
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(6)))
+w4a_kernel(const W4Args a) {   // 6 wavefronts per SIMD: 3 workgroups per CU, the 576 of the FLUX shape at once
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint32_t* tab = reinterpret_cast<uint32_t*>(smem);
+  float* red = reinterpret_cast<float*>(smem + kTabBytes);
+  unsigned char* xs = smem + kTabBytes + kRedBytes;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int lr = lane & 15, j = lane >> 4;
-  const int n0 = blockIdx.x * kTile;
-  const int64_t t0 = (int64_t)blockIdx.y * kTile;
+  const int n0 = blockIdx.x * kFeat;
+  const int64_t t0 = (int64_t)blockIdx.y * a.tt;
   const int K = a.K, N = a.N;
-  const int64_t T = a.T;
+  const int rows = a.T - t0 < a.tt ? (int)(a.T - t0) : a.tt;
+  const int xstride = 2 * K + 16;
 
+  // this wavefront's 128-wide chunks
+  const int C = K / 128;
+  const int c0 = (int)((int64_t)C * wave / kWaves), c1 = (int)((int64_t)C * (wave + 1) / kWaves);
+  const int cpg = a.group / 128;   // chunks per group
+
+  // weights of the first batch (HBM): issued first, the longest wait
+  int nf[2];
+  const uint8_t* qrow[2];
+  const float* srow[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    const int nn = n0 + 16 * f + lr;
+    nf[f] = nn < N ? nn : N - 1;
+    qrow[f] = a.q + (size_t)nf[f] * (K / 2) + j * 16;
+    srow[f] = a.scale + (size_t)nf[f] * (K / a.group);
+  }
+  u32x4 wq[kBatch][2];
+  float scl[kBatch][2];   // scale of each chunk's group, loaded with its codes
+  auto wload = [&](int cb) {
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int c = cb + i < c1 ? cb + i : c1 - 1;
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        wq[i][f] = *reinterpret_cast<const u32x4*>(qrow[f] + (size_t)c * 64);
+        scl[i][f] = srow[f][c / cpg];
+      }
+    }
+  };
+  if (c0 < c1) wload(c0);
+
+  // activation rows -> LDS (16-byte pieces), nibble-pair table
+  {
+    const uint16_t* xg = static_cast<const uint16_t*>(a.x) + (size_t)t0 * K;
+    const int per_row = K / 8, np = rows * per_row;
+    for (int p0 = 0; p0 < np; p0 += kThreads * 2) {
+      u32x4 v[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int p = p0 + tid + u * kThreads;
+        if (p < np) v[u] = *reinterpret_cast<const u32x4*>(xg + (size_t)p * 8);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int p = p0 + tid + u * kThreads;
+        if (p < np) *reinterpret_cast<u32x4*>(xs + (p / per_row) * xstride + (p % per_row) * 16) = v[u];
+      }
+    }
+  }
   if (tid < 256) {
     // byte e = (hi nibble, lo nibble) of two's-complement codes -> two exact 16-bit values
     const int lo = (tid & 15) - ((tid & 8) << 1), hi = (tid >> 4) - ((tid & 128) >> 3);
@@ -122,64 +183,54 @@ __global__ void __launch_bounds__(kThreads) w4a_kernel(const W4Args a) {
     }
     tab[tid] = vlo | (vhi << 16);
   }
+  __syncthreads();
 
-  const int n = n0 + lr < N ? n0 + lr : N - 1;
-  const int64_t t = t0 + lr;
-  const bool trow = t < T;
-  const uint8_t* qrow = a.q + (size_t)n * (K / 2) + j * 16;
-  const uint16_t* xrow = static_cast<const uint16_t*>(a.x) + (size_t)(trow ? t : 0) * K + j * 32;
-  const float* srow = a.scale + (size_t)n * (K / a.group);
-
-  // this wavefront's 128-wide chunks
-  const int C = K / 128;
-  const int c0 = (int)((int64_t)C * wave / kWaves), c1 = (int)((int64_t)C * (wave + 1) / kWaves);
-  const int cpg = a.group / 128;   // chunks per group
-
-  __syncthreads();   // table ready
-
-  f32x4 tot = f32x4{0.f, 0.f, 0.f, 0.f}, acc = tot;
+  const bool trow = lr < rows;
+  const unsigned char* xa = xs + lr * xstride + j * 64;
+  f32x4 tot[2], acc[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) tot[f] = acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int cb = c0; cb < c1; cb += kBatch) {
-    u32x4 wq[kBatch], xa[kBatch][4];
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const int c = cb + i < c1 ? cb + i : c1 - 1;
-      wq[i] = *reinterpret_cast<const u32x4*>(qrow + (size_t)c * 64);
-#pragma unroll
-      for (int st = 0; st < 4; ++st)
-        xa[i][st] = trow ? *reinterpret_cast<const u32x4*>(xrow + (size_t)c * 128 + 8 * st) : u32x4{0u, 0u, 0u, 0u};
-    }
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
       const int c = cb + i;
       if (c < c1) {
 #pragma unroll
-        for (int st = 0; st < 4; ++st) acc = mfma<BF16>(xa[i][st], decode8(tab, wq[i][st]), acc);
+        for (int st = 0; st < 4; ++st) {
+          const u32x4 av = trow ? *reinterpret_cast<const u32x4*>(xa + c * 256 + st * 16) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int f = 0; f < 2; ++f) acc[f] = mfma<BF16>(av, decode8(tab, wq[i][f][st]), acc[f]);
+        }
         // end of a group (or of this wavefront's range): scale it into the total
         if ((c + 1) % cpg == 0 || c + 1 == c1) {
-          const float sc = srow[c / cpg];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) tot[r] = fmaf(sc, acc[r], tot[r]);
-          acc = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int f = 0; f < 2; ++f) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) tot[f][r] = fmaf(scl[i][f], acc[f][r], tot[f][r]);
+            acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
         }
       }
     }
+    if (cb + kBatch < c1) wload(cb + kBatch);
   }
 
   // partial tiles -> LDS, then a fixed-order sum over the wavefronts
-  const int rows = T - t0 < kTile ? (int)(T - t0) : kTile;
-  float* rw = red + wave * kTile * kRedStride;
+  float* rw = red + wave * 16 * kRedStride;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = 4 * j + r;
-    if (row < rows) rw[row * kRedStride + lr] = tot[r];
-  }
+  for (int f = 0; f < 2; ++f)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * j + r;
+      if (row < rows) rw[row * kRedStride + 16 * f + lr] = tot[f][r];
+    }
   __syncthreads();
-  for (int e = tid; e < rows * kTile; e += kThreads) {
-    const int row = e / kTile, col = e % kTile;
+  for (int e = tid; e < rows * kFeat; e += kThreads) {
+    const int row = e / kFeat, col = e % kFeat;
     if (n0 + col >= N) continue;
     float v = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) v += red[(w * kTile + row) * kRedStride + col];
+    for (int w = 0; w < kWaves; ++w) v += red[(w * 16 + row) * kRedStride + col];
     if (a.bias) v += a.bias[n0 + col];
     a.y[(size_t)(t0 + row) * N + n0 + col] = v;
   }
@@ -197,13 +248,29 @@ hipError_t rtn_launch(const RtnArgs& a, bool bf16, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t w4a_launch(const W4Args& a, bool bf16, hipStream_t st) {
-  if (a.T == 0 || a.N == 0) return hipSuccess;
-  const int64_t gy = (a.T + kTile - 1) / kTile;   // token tiles
+hipError_t w4a_launch(const W4Args& a_in, bool bf16, hipStream_t st) {
+  if (a_in.T == 0 || a_in.N == 0) return hipSuccess;
+  W4Args a = a_in;
+  // tokens per workgroup: up to the 16 rows of the MFMA tile, as many as fit the LDS
+  const int xstride = 2 * a.K + 16;
+  const int64_t fit = kXLdsMax / xstride;
+  if (fit < 1) return hipErrorInvalidValue;
+  a.tt = (int)(fit < 16 ? fit : 16);
+  const int64_t tt = a.tt < a.T ? a.tt : a.T;
+  const int64_t gy = (a.T + a.tt - 1) / a.tt;   // token tiles
   if (gy > 65535) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)((a.N + kTile - 1) / kTile), (unsigned)gy);
-  if (bf16) hipLaunchKernelGGL(w4a_kernel<true>, grid, dim3(kThreads), 0, st, a);
-  else hipLaunchKernelGGL(w4a_kernel<false>, grid, dim3(kThreads), 0, st, a);
+  const size_t lds = kTabBytes + kRedBytes + (size_t)tt * xstride;
+  static thread_local bool raised[2] = {false, false};
+  if (!raised[bf16]) {
+    const void* fn = bf16 ? (const void*)w4a_kernel<true> : (const void*)w4a_kernel<false>;
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       kTabBytes + kRedBytes + kXLdsMax);
+    if (e != hipSuccess) return e;
+    raised[bf16] = true;
+  }
+  const dim3 grid((unsigned)((a.N + kFeat - 1) / kFeat), (unsigned)gy);
+  if (bf16) hipLaunchKernelGGL(w4a_kernel<true>, grid, dim3(kThreads), lds, st, a);
+  else hipLaunchKernelGGL(w4a_kernel<false>, grid, dim3(kThreads), lds, st, a);
   return hipGetLastError();
 }
 
