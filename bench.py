@@ -210,8 +210,9 @@ def modulation_line(name, lin, r):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps first: the GPU clock ramps over the first ~60 ms of work")
     ap.add_argument("--workload", default="flux_qkv_w4a4")
     ap.add_argument("--ring-mb", type=float, default=640.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
