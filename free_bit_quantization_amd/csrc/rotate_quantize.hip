@@ -26,9 +26,9 @@
 //      recomputed in fp64 by the wavefront (rare) before its index is set;
 //   6. LSB-first packing of 2 / 4 / 8-bit indices, one 4 / 8 / 16-byte store.
 //
-// Rows of d = 1024 J coordinates (J <= 3) with h = 64 or 256 take a second
-// mapping of the same steps, rq_wave_kernel: a wavefront owns whole tokens
-// (48 coordinates per lane at J = 3), so no workgroup barrier is needed after
+// Rows of d = 1024 J coordinates (J <= 5 for bf16, <= 2 for fp32) with h = 64
+// or 256 take a second mapping of the same steps, rq_wave_kernel: a wavefront
+// owns whole tokens (16 J coordinates per lane), so no workgroup barrier is needed after
 // the set-up and every wavefront keeps its own token row in flight.
 //
 // Weight kernel (offline): one workgroup per row, fp64 throughout.
@@ -465,7 +465,7 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
   }
 }
 
-// ---- activations, one wavefront per token (d = 1024 J, J <= 3, h = 64 or 256) ----
+// ---- activations, one wavefront per token (d = 1024 J, J <= 5, h = 64 or 256) ----
 // The same computation as rq_act_kernel with a different mapping: a
 // wavefront owns whole tokens, lane l stages the 16-coordinate chunks
 // l, l + 64, ... of the row (coalesced), the norm is a wavefront sum, and
@@ -497,7 +497,7 @@ __host__ __device__ inline RqwLayout rqw_layout(int d, int log2h, int es, int G,
 }
 
 template <int LOG2H, bool BF16, int BITS, int J>
-__global__ void __launch_bounds__(768) rq_wave_kernel(const RqArgs a, const int WPB) {
+__global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArgs a, const int WPB) {
   constexpr int H = 1 << LOG2H;
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int BL = H / 16;                       // lanes per Hadamard block (h >= 32: two passes)
@@ -547,7 +547,7 @@ __global__ void __launch_bounds__(768) rq_wave_kernel(const RqArgs a, const int 
   // offset perm(gin) * ES sits at atab[((4 j + r / 4) * 64 + l) * 4 + r % 4], so
   // a slot's 16 offsets are four conflict-free 16-byte reads per lane
   auto gin = [&](int j, int l, int r) { return 1024 * j + (l / BL) * H + r * BL + (l % BL); };
-  // d <= 4096 and blockDim >= 256: at most 16 entries per thread
+  // d <= 16 blockDim (checked by the plan): at most 16 entries per thread
   int pj[16], pa[16];
   int8_t sj[16];
 #pragma unroll
@@ -935,6 +935,12 @@ hipError_t rqw_dispatch_j(const RqArgs& a, const RqPlan& p, hipStream_t st) {
     case 3:
       if constexpr (BF16) return rqw_go<LOG2H, BF16, BITS, 3>(a, p, st);
       else return hipErrorInvalidValue;
+    case 4:
+      if constexpr (BF16) return rqw_go<LOG2H, BF16, BITS, 4>(a, p, st);
+      else return hipErrorInvalidValue;
+    case 5:
+      if constexpr (BF16) return rqw_go<LOG2H, BF16, BITS, 5>(a, p, st);
+      else return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
 }
@@ -966,15 +972,18 @@ bool rq_plan(int32_t d, int32_t log2h, bool bf16, int64_t T, int G, RqPlan* p) {
   const int ns = d / 16;
   p->wave_j = 0;
   p->wpb = 0;
-  // one wavefront per token: d = 1024 J with J <= 3 (bf16) or J <= 2 (fp32: the
+  // one wavefront per token: d = 1024 J with J <= 5 (bf16) or J <= 2 (fp32: the
   // prefetched row takes twice the registers), h in {64, 256}, grid search
-  if (ns % 64 == 0 && ns / 64 <= (bf16 ? 3 : 2) && (log2h == 6 || log2h == 8) && G > 0) {
+  if (ns % 64 == 0 && ns / 64 <= (bf16 ? 5 : 2) && (log2h == 6 || log2h == 8) && G > 0) {
     const int J = ns / 64;
     const int es = bf16 ? 2 : 4;
-    int wpb = 12;   // 768 threads: 3 wavefronts per SIMD (the kernel's register budget)
+    // J <= 3: 768 threads, 3 wavefronts per SIMD; J = 4, 5: 512 threads (the
+    // kernels' register budgets); fewer if the row buffers exceed the LDS
+    int wpb = J <= 3 ? 12 : 8;
     while (wpb > 4 && rqw_layout(d, log2h, es, G, wpb).total > 160 * 1024) wpb -= 4;
     const RqwLayout L = rqw_layout(d, log2h, es, G, wpb);
-    if (L.total <= 160 * 1024) {
+    // the set-up gives each thread at most 16 of the d table entries: 64 wpb >= d / 16
+    if (L.total <= 160 * 1024 && 64 * wpb * 16 >= d) {
       p->ns = ns;
       p->tpw = 1;
       p->wave_j = J;

@@ -107,7 +107,9 @@ def test_block_rht_tables_through_both_kernels():
 
 @pytest.mark.parametrize("d,h,dtype", [(256, 2, "f32"), (256, 4, "bf16"), (256, 16, "f32"), (512, 32, "bf16"),
                                        (1024, 64, "f32"), (1024, 128, "bf16"), (2048, 256, "bf16"),
-                                       (64, 64, "f32"), (16, 16, "bf16"), (12288, 256, "f32")])
+                                       (64, 64, "f32"), (16, 16, "bf16"), (12288, 256, "f32"),
+                                       (4096, 256, "bf16"), (5120, 64, "bf16"), (5120, 256, "bf16"),
+                                       (4096, 64, "f32")])
 @pytest.mark.parametrize("bits", [2, 3, 4, 6, 8])
 def test_rotate_quantize_shapes_and_widths(d, h, dtype, bits):
     rng = np.random.default_rng(d * 7 + h + bits)
