@@ -21,9 +21,13 @@
 //      hold at most one threshold, so idx = base[cell] + (u > theta[cell]),
 //      decided by the sign of one fma;
 //   5. guard: a coordinate whose fp32 value lies within a certified rounding
-//      bound of its threshold (2 (log2 h + 1) 2^-24 L1(block) / (sqrt(h) s)
-//      for the butterflies, plus 16 ulp of |theta| for s and the scaling) is
-//      recomputed in fp64 by the wavefront (rare) before its index is set;
+//      bound of its threshold is recomputed in fp64 by the wavefront (rare)
+//      before its index is set.  Bound: each output of the m = log2 h
+//      butterfly stages is a depth-m tree of +-sums of exact inputs, so its
+//      error is at most gamma_m L1(block), gamma_m = m u / (1 - m u), u = 2^-24;
+//      the guard uses (m + 1) u L1 / (sqrt(h) s) with L1 and s as computed
+//      (their relative errors, below 3e-5, fit in the extra u), plus 16 ulp
+//      of |theta| for the rounding of s, of the scale and of theta to fp32;
 //   6. LSB-first packing of 2 / 4 / 8-bit indices, one 4 / 8 / 16-byte store.
 //
 // Rows of d = 1024 J coordinates (J <= 5 for bf16, <= 2 for fp32) with h = 64
@@ -181,7 +185,7 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
   constexpr bool TWO_PASS = LOG2H > 4;
   constexpr int BL = TWO_PASS ? H / 16 : 1;        // lanes per Hadamard block
   constexpr int BPL = TWO_PASS ? 1 : 16 / H;       // Hadamard blocks per lane (one pass)
-  constexpr float kGam = 2.0f * (LOG2H + 1) * 5.9604644775390625e-8f;  // 2 (m+1) 2^-24
+  constexpr float kGam = (LOG2H + 1) * 5.9604644775390625e-8f;  // (m+1) 2^-24 > gamma_m (1 + 3e-5)
   constexpr float kRel = 16.0f * 5.9604644775390625e-8f;               // 16 ulp of |theta|
 
   const int d = a.d;
@@ -502,7 +506,7 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int BL = H / 16;                       // lanes per Hadamard block (h >= 32: two passes)
   static_assert(LOG2H >= 5 && LOG2H <= 8, "two-pass block sizes only");
-  constexpr float kGam = 2.0f * (LOG2H + 1) * 5.9604644775390625e-8f;  // 2 (m+1) 2^-24
+  constexpr float kGam = (LOG2H + 1) * 5.9604644775390625e-8f;  // (m+1) 2^-24 > gamma_m (1 + 3e-5)
   constexpr float kRel = 16.0f * 5.9604644775390625e-8f;               // 16 ulp of |theta|
   constexpr int NV = BF16 ? 2 : 4;                 // 16-byte loads per 16-coordinate chunk
   constexpr int MW = BF16 ? 8 : 16;                // sign-mask words per chunk
