@@ -175,6 +175,15 @@ def test_gemm_non_byte_index_widths(bits_w, bits_a, T, d, d_out, h):
     run_linear(lin, bias=True, seed=bits_w * 10 + bits_a)
 
 
+@pytest.mark.parametrize("bits_w,bits_a,T,d,d_out,h", [(2, 8, 300, 1024, 260, 256), (4, 4, 70, 1024, 258, 64),
+                                                      (2, 4, 33, 512, 131, 32), (4, 8, 129, 3072, 517, 256)])
+def test_gemm_byte_widths_ragged_columns(bits_w, bits_a, T, d, d_out, h):
+    # W2A8 and d_out not a multiple of 4 (the per-element store path of the epilogue)
+    lin = synth.Linear(f"w{bits_w}a{bits_a}r", T, d, d_out, h, bits_w, bits_a, "student_t", "bf16", 10, 30.0, 0.5,
+                       5, 10.0)
+    run_linear(lin, bias=True, seed=bits_w * 100 + d_out)
+
+
 def test_gemm_repeatable():
     lin = W["single_w4a4_64x256x256"].linears[0]
     x, Wm = synth.gen_linear(lin, 0, 0)
