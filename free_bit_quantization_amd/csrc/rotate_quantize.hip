@@ -982,8 +982,10 @@ bool rq_plan(int32_t d, int32_t log2h, bool bf16, int64_t T, int G, RqPlan* p) {
     const int J = ns / 64;
     const int es = bf16 ? 2 : 4;
     // J <= 3: 768 threads, 3 wavefronts per SIMD; J = 4, 5: 512 threads (the
-    // kernels' register budgets); fewer if the row buffers exceed the LDS
-    int wpb = J <= 3 ? 12 : 8;
+    // kernels' register budgets); fewer if the row buffers exceed the LDS.
+    // Below 3072 tokens 8 wavefronts per workgroup spread the tokens over more
+    // CUs (measured ~1 us faster at 256-1024 tokens, slower from 4608 on).
+    int wpb = J <= 3 && T >= 3072 ? 12 : 8;
     while (wpb > 4 && rqw_layout(d, log2h, es, G, wpb).total > 160 * 1024) wpb -= 4;
     const RqwLayout L = rqw_layout(d, log2h, es, G, wpb);
     // the set-up gives each thread at most 16 of the d table entries: 64 wpb >= d / 16
