@@ -167,6 +167,20 @@ oq_status oq_rotate_quantize_act(const void* x, oq_dtype x_dtype, int64_t T, int
   a.g_invw = G > 0 ? G / (hi - lo) : 0.0;
   a.g_rmax = rmax;
   for (int i = 0; i < nthr; ++i) a.thr[i] = th32[i];
+  if (G > 0 && G <= oq::kHostGrid) {
+    // cell c covers u in [lo + (c - 0.02) w - rmax, lo + (c + 1.02) w + rmax]: the
+    // number of thresholds below it and the one threshold inside it (or +inf)
+    const double w = 1.0 / a.g_invw;
+    for (int c = 0; c < G; ++c) {
+      const double ulo = c == 0 ? -INFINITY : lo + (c - 0.02) * w - rmax;
+      const double uhi = c == G - 1 ? INFINITY : lo + (c + 1.02) * w + rmax;
+      int base = 0;
+      while (base < nthr && (double)th32[base] < ulo) ++base;
+      const float th = (base < nthr && (double)th32[base] <= uhi) ? th32[base] : INFINITY;
+      std::memcpy(&a.glut[c][0], &th, 4);
+      a.glut[c][1] = base;
+    }
+  }
   hipError_t e = oq::rq_launch(a, x_dtype == OQ_BF16, bits_a, plan, stream);
   if (e != hipSuccess) return device_error(e, "oq_rotate_quantize_act launch");
   return ok();

@@ -18,6 +18,7 @@ int lloyd_max_fd(int d, int bits, double* centroids, double* thresholds, double*
 // ---- rotate-quantize (activations, fp32 fast path + fp64 recheck) ------------
 constexpr int kMaxThr = 255;     // 2^8 - 1 thresholds
 constexpr int kMaxGrid = 4096;   // cells of the threshold-search grid
+constexpr int kHostGrid = 64;    // grids up to this size are built on the host (RqArgs::glut)
 
 struct RqArgs {
   const void* x;
@@ -35,6 +36,7 @@ struct RqArgs {
   double g_invw;     // cells per unit u
   double g_rmax;     // widening of each cell for the recheck guard (u units)
   float thr[kMaxThr];
+  int32_t glut[kHostGrid][2];   // G <= kHostGrid: cell c -> {bits of its threshold (or +inf), thresholds below it}
 };
 
 // Plan of a launch, chosen on the host from (d, h, dtype, bits, T).

@@ -26,8 +26,10 @@
 //      butterfly stages is a depth-m tree of +-sums of exact inputs, so its
 //      error is at most gamma_m L1(block), gamma_m = m u / (1 - m u), u = 2^-24;
 //      the guard uses (m + 1) u L1 / (sqrt(h) s) with L1 and s as computed
-//      (their relative errors, below 3e-5, fit in the extra u), plus 16 ulp
-//      of |theta| for the rounding of s, of the scale and of theta to fp32;
+//      (their relative errors, below 3e-5, fit in the extra u), plus 6 u
+//      max|theta| for the scale c = 1 / (sqrt(h) (s + eps)) (at most ~3.3 u
+//      relative: fp32 ss, sqrt, +eps, division; sqrt(h) exact or c rounded
+//      once from fp64) and theta's rounding to fp32 (0.5 u), at |u| ~ |theta|;
 //   6. LSB-first packing of 2 / 4 / 8-bit indices, one 4 / 8 / 16-byte store.
 //
 // Rows of d = 1024 J coordinates (J <= 5 for bf16, <= 2 for fp32) with h = 64
@@ -186,7 +188,7 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
   constexpr int BL = TWO_PASS ? H / 16 : 1;        // lanes per Hadamard block
   constexpr int BPL = TWO_PASS ? 1 : 16 / H;       // Hadamard blocks per lane (one pass)
   constexpr float kGam = (LOG2H + 1) * 5.9604644775390625e-8f;  // (m+1) 2^-24 > gamma_m (1 + 3e-5)
-  constexpr float kRel = 16.0f * 5.9604644775390625e-8f;               // 16 ulp of |theta|
+  constexpr float kRel = 6.0f * 5.9604644775390625e-8f;   // 6 ulp of |theta| >= 2x the scale + theta roundings
 
   const int d = a.d;
   const int tid = threadIdx.x;
@@ -507,7 +509,7 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
   constexpr int BL = H / 16;                       // lanes per Hadamard block (h >= 32: two passes)
   static_assert(LOG2H >= 5 && LOG2H <= 8, "two-pass block sizes only");
   constexpr float kGam = (LOG2H + 1) * 5.9604644775390625e-8f;  // (m+1) 2^-24 > gamma_m (1 + 3e-5)
-  constexpr float kRel = 16.0f * 5.9604644775390625e-8f;               // 16 ulp of |theta|
+  constexpr float kRel = 6.0f * 5.9604644775390625e-8f;   // 6 ulp of |theta| >= 2x the scale + theta roundings
   constexpr int NV = BF16 ? 2 : 4;                 // 16-byte loads per 16-coordinate chunk
   constexpr int MW = BF16 ? 8 : 16;                // sign-mask words per chunk
   constexpr int d = 1024 * J;
@@ -578,7 +580,9 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
     }
   }
   __syncthreads();
-  if (G > 0) {
+  if (G > 0 && G <= kHostGrid) {
+    for (int c = tid; c < G; c += blockDim.x) lut[c] = make_int2(a.glut[c][0], a.glut[c][1]);   // built on the host
+  } else if (G > 0) {
     const double w = 1.0 / a.g_invw;
     for (int c = tid; c < G; c += blockDim.x) {
       const double ulo = c == 0 ? -INFINITY : a.g_lo + (c - 0.02) * w - a.g_rmax;
@@ -720,7 +724,10 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
         }
       }
 
-      // fp64 recheck of guarded coordinates, by the whole wavefront (rare)
+      // fp64 recheck of guarded coordinates (rare).  The BL lanes of a Hadamard
+      // block hold its inputs (pass 1) and its outputs (pass 2), so each group
+      // of BL lanes recomputes one of its flagged coordinates per round, all
+      // groups at once, with an fp64 sum over the group.
       if (__ballot(near) != 0) {
         uint32_t flags = 0;
         if (near) {
@@ -731,12 +738,23 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
             flags |= (nr ? 1u : 0u) << r;
           }
         }
+        const double inv64 = 1.0 / (sqrt((double)H) * (sqrt(ss) + OQ_EPS));
+        const int g0 = lane & ~(BL - 1);   // first lane of this lane's block group
+        // the gather addresses again (not kept live through the transform)
+        uint32_t raddr[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x4 o = reinterpret_cast<const u32x4*>(atab)[(4 * j + q) * 64 + lane];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) raddr[4 * q + k] = rowbase + o[k];
+        }
         while (true) {
           const uint64_t bal = __ballot(flags != 0);
           if (bal == 0) break;
-          const int L = __ffsll((unsigned long long)bal) - 1;
+          const uint32_t gm = (uint32_t)(bal >> g0) & ((1u << BL) - 1u);   // flagged lanes of the group
+          const int L = gm ? g0 + __ffs(gm) - 1 : lane;                    // owner of this round's coordinate
           const uint32_t fl = __shfl(flags, L);
-          const int r = __ffs(fl) - 1;
+          const int r = gm ? __ffs(fl) - 1 : 0;
           const int gi = 1024 * j + 16 * L + r;   // coordinate of pass-2 element r of lane L
           const int b = gi >> LOG2H;
           const int jj = gi & (H - 1);
@@ -744,16 +762,16 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) {
             const int gk = gin(j, lane, rr);
-            if ((gk >> LOG2H) == b) {
+            if (gm && (gk >> LOG2H) == b) {
               double yv;
-              if (BF16) yv = (double)__uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t*>(smem + addr[rr])) << 16);
-              else yv = (double)*reinterpret_cast<const float*>(smem + addr[rr]);
+              if (BF16) yv = (double)__uint_as_float((uint32_t)(*reinterpret_cast<const uint16_t*>(smem + raddr[rr])) << 16);
+              else yv = (double)*reinterpret_cast<const float*>(smem + raddr[rr]);
               part += (__popc(jj & gk & (H - 1)) & 1) ? -yv : yv;
             }
           }
-          part = wave_sum_d(part);
-          if (lane == L) {
-            const double u = part / (sqrt((double)H) * (sqrt(ss) + OQ_EPS));
+          part = group_sum<BL>(part);
+          if (gm && lane == L) {
+            const double u = part * inv64;
             // u is exact here: its cell holds the only threshold that can lie in it
             const double cf = fmin(fmax(floor((u - a.g_lo) * a.g_invw), 0.0), (double)(G - 1));
             const int2 e = lut[(int)cf];

@@ -228,3 +228,43 @@ def test_full_wan_ffn_w4a4():
 def test_full_flux_block_w4a8():
     for k, lin in enumerate(W["flux_block_w4a8_b2"].linears):
         run_linear(lin, index=k, act_rows=_sample_rows(lin.T, 256), gemm_rows=_sample_rows(lin.T, 32))
+
+
+# ---- the certified guard under pressure: coordinates placed at the thresholds ----
+
+
+@pytest.mark.parametrize("d,h,bits", [(1024, 256, 4), (3072, 256, 4), (2048, 64, 2), (3072, 256, 8)])
+def test_guard_with_coordinates_at_thresholds(d, h, bits):
+    # Rows built in the rotated basis: a quarter of the normalised coordinates
+    # sit within +-3e-8 (relative) of a threshold, the rest are N(0, 1/d)
+    # rescaled so each row has unit norm; x = R^T x_rot in fp64, rounded to fp32.
+    # Many coordinates then fall inside the guard band (several per Hadamard
+    # block), so the fp64 recheck decides them; the oracle judges every index.
+    from oracle import rpbh
+    rng = np.random.default_rng(d + h + bits)
+    T = 64
+    perm, sign, _, _ = P.rotation(d, h, 0, "rpbh")
+    th = P.library_codebook(d, bits).th
+    u = rng.standard_normal((T, d)) / np.sqrt(d)
+    mask = rng.random((T, d)) < 0.25
+    k = rng.integers(0, len(th), (T, d))
+    delta = rng.choice(np.array([-3e-8, -1e-8, -1e-9, 1e-9, 1e-8, 3e-8]), (T, d))
+    u = np.where(mask, th[k] * (1.0 + delta), u)
+    placed = (u * mask) ** 2
+    free = (u * ~mask) ** 2
+    scale = np.sqrt((1.0 - placed.sum(axis=1)) / free.sum(axis=1))
+    u = np.where(mask, u, u * scale[:, None])
+    x_rot = 3.0 * u
+    # inverse rotation: R = B D P with B symmetric, so x[perm] = sign * (B x_rot)
+    z = rpbh.rotate(x_rot, np.arange(d), np.ones(d, dtype=np.int8), h)   # B x_rot
+    x = np.empty_like(z)
+    x[:, perm] = sign[None, :] * z
+    x = x.astype(np.float32)
+    _, _, rep = P.check_activations(x, "f32", h, bits, want_x_rot=False, name=f"guard-{d}-{h}-{bits}")
+    _assert_act(rep)
+    # the case has to reach the guard: count coordinates of the oracle's exact
+    # rotation that lie within 1e-6 of a threshold
+    xo = rpbh.rotate(x.astype(np.float64), perm, sign, h)
+    uo = xo / np.linalg.norm(xo, axis=1, keepdims=True)
+    near = np.min(np.abs(uo[:, :, None] - th[None, None, :]), axis=2) < 1e-6
+    assert near.sum() > T * d // 20, near.sum()
