@@ -36,7 +36,7 @@ FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, TFLOP/s
 # for the kernel source they were taken on (sha256 prefix); otherwise null.
 MEASURED_TRAFFIC = {
     "free_bit_quantization_amd/csrc/qlinear.hip": ("9ae076693d65c2db", 125.7e6, 169.9e6),
-    "free_bit_quantization_amd/csrc/rotate_quantize.hip": ("76ca9fb0707437e7", 28.8e6, 7.2e6),
+    "free_bit_quantization_amd/csrc/rotate_quantize.hip": ("1feb412e40dc2196", 28.9e6, 7.2e6),
 }
 
 

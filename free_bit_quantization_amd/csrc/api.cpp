@@ -138,7 +138,10 @@ oq_status oq_rotate_quantize_act(const void* x, oq_dtype x_dtype, int64_t T, int
 
   // Threshold-search grid: cells of width w over [theta_0, theta_{L-2}], each
   // widened by 0.02 w (rounding of the cell index) and by the largest guard
-  // radius, must hold at most one threshold.
+  // radius, must hold at most one threshold.  The radius is at most
+  // (m + 1) u L1 c + k u max|theta| with L1 c <= 1 (Cauchy-Schwarz over a
+  // block), max|theta| < 1 and k = 6 (workgroup kernel) or 4 J + 5 <= 25
+  // (wavefront kernel, m >= 6): below (2 m + 24) u, u = 2^-24.
   float th32[oq::kMaxThr];
   for (int i = 0; i < nthr; ++i) th32[i] = (float)thresholds[i];
   const double lo = th32[0], hi = th32[nthr - 1];
@@ -166,7 +169,10 @@ oq_status oq_rotate_quantize_act(const void* x, oq_dtype x_dtype, int64_t T, int
   a.g_lo = lo;
   a.g_invw = G > 0 ? G / (hi - lo) : 0.0;
   a.g_rmax = rmax;
-  for (int i = 0; i < nthr; ++i) a.thr[i] = th32[i];
+  for (int i = 0; i < nthr; ++i) {
+    a.thr[i] = th32[i];
+    a.thr_lo[i] = (float)(thresholds[i] - (double)th32[i]);   // the difference is exact in fp64
+  }
   if (G > 0 && G <= oq::kHostGrid) {
     // cell c covers u in [lo + (c - 0.02) w - rmax, lo + (c + 1.02) w + rmax]: the
     // number of thresholds below it and the one threshold inside it (or +inf)

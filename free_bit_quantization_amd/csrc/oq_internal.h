@@ -36,6 +36,7 @@ struct RqArgs {
   double g_invw;     // cells per unit u
   double g_rmax;     // widening of each cell for the recheck guard (u units)
   float thr[kMaxThr];
+  float thr_lo[kMaxThr];         // threshold - thr, rounded to fp32: thr + thr_lo is the fp64 threshold to 2^-48
   int32_t glut[kHostGrid][2];   // G <= kHostGrid: cell c -> {bits of its threshold (or +inf), thresholds below it}
 };
 

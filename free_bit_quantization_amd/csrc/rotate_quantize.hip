@@ -11,7 +11,8 @@
 // each lane owning 16 coordinates:
 //   1. coalesced 16-byte loads of the row into LDS (double-buffered across
 //      loop iterations) and the sum of squares: s = ||x|| = ||x_rot|| since R
-//      is orthogonal; per-lane fp32 partials, fp64 across lanes;
+//      is orthogonal; per-lane fp64 sums of the exact squares (the
+//      wavefront mapping below: fp32 per lane), fp64 across lanes;
 //   2. signed gather from LDS: lane holds y_r = sign[i_r] x[perm[i_r]]; the
 //      16 LDS addresses and sign words are loop-invariant registers;
 //   3. block FWHT: a 16-point in-register transform over the top 4 index
@@ -22,14 +23,18 @@
 //      decided by the sign of one fma;
 //   5. guard: a coordinate whose fp32 value lies within a certified rounding
 //      bound of its threshold is recomputed in fp64 by the wavefront (rare)
-//      before its index is set.  Bound: each output of the m = log2 h
+//      and compared with the fp64 threshold (fp32 value + fp32 residual)
+//      before its index is set, so every index is the one exact arithmetic
+//      gives, up to fp64 rounding.  Bound: each output of the m = log2 h
 //      butterfly stages is a depth-m tree of +-sums of exact inputs, so its
 //      error is at most gamma_m L1(block), gamma_m = m u / (1 - m u), u = 2^-24;
 //      the guard uses (m + 1) u L1 / (sqrt(h) s) with L1 and s as computed
-//      (their relative errors, below 3e-5, fit in the extra u), plus 6 u
-//      max|theta| for the scale c = 1 / (sqrt(h) (s + eps)) (at most ~3.3 u
-//      relative: fp32 ss, sqrt, +eps, division; sqrt(h) exact or c rounded
-//      once from fp64) and theta's rounding to fp32 (0.5 u), at |u| ~ |theta|;
+//      (their relative errors fit in the extra u), plus k u max|theta| for the
+//      scale c = 1 / (sqrt(h) (s + eps)) and theta's rounding to fp32 (u), at
+//      |u| ~ |theta|: k = 6 where s comes from fp64 sums of the exact squares
+//      (c rounded once from fp64), k = 4 J + 5 where the fast path sums 8 J
+//      squares per lane in fp32 ((8 J + 1) u in s^2, (4 J + 3.5) u in c); the
+//      recheck then takes s from fp64 squares of the staged row;
 //   6. LSB-first packing of 2 / 4 / 8-bit indices, one 4 / 8 / 16-byte store.
 //
 // Rows of d = 1024 J coordinates (J <= 5 for bf16, <= 2 for fp32) with h = 64
@@ -180,6 +185,16 @@ __device__ __forceinline__ int count_below_f64(const float* thr, int n, double u
   return lo;
 }
 
+// #{j : theta_j < u} against the fp64 thresholds theta_j = thr[j] + thr_lo[j]
+// (the sum is exact in fp64: thr_lo lies below half an fp32 ulp of thr)
+__device__ __forceinline__ int count_below_exact(const float* thr, const float* thr_lo, int n, double u) {
+  int lo = 0;
+#pragma unroll
+  for (int step = 128; step >= 1; step >>= 1)
+    if (lo + step <= n && (double)thr[lo + step - 1] + (double)thr_lo[lo + step - 1] < u) lo += step;
+  return lo;
+}
+
 template <int LOG2H, bool BF16, int BITS>
 __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int NS, const int TPW) {
   constexpr int H = 1 << LOG2H;
@@ -188,7 +203,7 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
   constexpr int BL = TWO_PASS ? H / 16 : 1;        // lanes per Hadamard block
   constexpr int BPL = TWO_PASS ? 1 : 16 / H;       // Hadamard blocks per lane (one pass)
   constexpr float kGam = (LOG2H + 1) * 5.9604644775390625e-8f;  // (m+1) 2^-24 > gamma_m (1 + 3e-5)
-  constexpr float kRel = 6.0f * 5.9604644775390625e-8f;   // 6 ulp of |theta| >= 2x the scale + theta roundings
+  constexpr float kRel = 6.0f * 5.9604644775390625e-8f;   // 6 ulp of |theta| >= 2x the scale (one rounding from fp64) + theta roundings
 
   const int d = a.d;
   const int tid = threadIdx.x;
@@ -260,7 +275,7 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
     const uint32_t paroff = par * (uint32_t)Ly.row_stride;
 
     // ---- 1. stage the prefetched coordinates [16 sl, 16 sl + 16), sum of squares
-    float q0 = 0.f, q1 = 0.f, q2 = 0.f, q3 = 0.f;
+    double q0 = 0.0, q1 = 0.0, q2 = 0.0, q3 = 0.0;   // exact squares, fp64 sums
     {
       u32x4* rowdst = reinterpret_cast<u32x4*>(smem + Ly.row + paroff + ((size_t)tl * d + 16 * sl) * ES);
 #pragma unroll
@@ -273,10 +288,10 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
             const uint32_t w0 = raw[k][q], w1 = raw[k][q + 1];
             const float e0 = __uint_as_float(w0 << 16), e1 = __uint_as_float(w0 & 0xFFFF0000u);
             const float e2 = __uint_as_float(w1 << 16), e3 = __uint_as_float(w1 & 0xFFFF0000u);
-            q0 = fmaf(e0, e0, q0);
-            q1 = fmaf(e1, e1, q1);
-            q2 = fmaf(e2, e2, q2);
-            q3 = fmaf(e3, e3, q3);
+            q0 = fma((double)e0, (double)e0, q0);
+            q1 = fma((double)e1, (double)e1, q1);
+            q2 = fma((double)e2, (double)e2, q2);
+            q3 = fma((double)e3, (double)e3, q3);
           }
         }
       } else {
@@ -284,16 +299,16 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
         for (int k = 0; k < 4; ++k) {
           const float e0 = __uint_as_float(raw[k][0]), e1 = __uint_as_float(raw[k][1]);
           const float e2 = __uint_as_float(raw[k][2]), e3 = __uint_as_float(raw[k][3]);
-          q0 = fmaf(e0, e0, q0);
-          q1 = fmaf(e1, e1, q1);
-          q2 = fmaf(e2, e2, q2);
-          q3 = fmaf(e3, e3, q3);
+          q0 = fma((double)e0, (double)e0, q0);
+          q1 = fma((double)e1, (double)e1, q1);
+          q2 = fma((double)e2, (double)e2, q2);
+          q3 = fma((double)e3, (double)e3, q3);
         }
       }
     }
     // the next token's row is in flight while this one is processed
     if (g + gridDim.x < ngroups) fetch(g + gridDim.x);
-    double ss = (double)((q0 + q1) + (q2 + q3));
+    double ss = (q0 + q1) + (q2 + q3);
     if (NS >= 64) {
       ss = wave_sum_d(ss);
       if (lane == 0) red[par * 16 + wave] = ss;
@@ -450,7 +465,7 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
       part = wave_sum_d(part);
       if (lane == L) {
         const double u = part / (sqrt((double)H) * (s64 + OQ_EPS));
-        pk.set(r, (uint32_t)count_below_f64(thr, nthr, u));
+        pk.set(r, (uint32_t)count_below_exact(thr, a.thr_lo, nthr, u));
         flags &= ~(1u << r);
       }
     }
@@ -509,7 +524,9 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
   constexpr int BL = H / 16;                       // lanes per Hadamard block (h >= 32: two passes)
   static_assert(LOG2H >= 5 && LOG2H <= 8, "two-pass block sizes only");
   constexpr float kGam = (LOG2H + 1) * 5.9604644775390625e-8f;  // (m+1) 2^-24 > gamma_m (1 + 3e-5)
-  constexpr float kRel = 6.0f * 5.9604644775390625e-8f;   // 6 ulp of |theta| >= 2x the scale + theta roundings
+  // the fast-path scale comes from per-lane fp32 sums of 8 J squares: relative
+  // error (8 J + 1) u in ss, (4 J + 3.5) u in c; with theta's rounding, (4 J + 5) u
+  constexpr float kRel = (4 * J + 5) * 5.9604644775390625e-8f;
   constexpr int NV = BF16 ? 2 : 4;                 // 16-byte loads per 16-coordinate chunk
   constexpr int MW = BF16 ? 8 : 16;                // sign-mask words per chunk
   constexpr int d = 1024 * J;
@@ -636,7 +653,7 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
     // registers free again: the next token's row is in flight from here on
     if (tok + nwaves < T) fetch(tok + nwaves);
     const double ss = wave_sum_d((double)(q0 + q1));
-    // fp32 scale for the fast path (a few ulp, inside the guard's 16 ulp of |theta|)
+    // fp32 scale for the fast path (its error is inside the guard's kRel)
     const float s32 = sqrtf((float)ss);
     const float c = 1.0f / (kSqrtH * (s32 + (float)OQ_EPS));
     const float cg = c * ginvw;
@@ -738,7 +755,30 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
             flags |= (nr ? 1u : 0u) << r;
           }
         }
-        const double inv64 = 1.0 / (sqrt((double)H) * (sqrt(ss) + OQ_EPS));
+        // the norm again, exactly: fp64 squares of the staged row (sign flips do
+        // not change them); the fast path's fp32 partials are only certified
+        double sx = 0.0;
+#pragma unroll
+        for (int i = 0; i < J; ++i) {
+          const u32x4* src = reinterpret_cast<const u32x4*>(wrow + (size_t)16 * (lane + 64 * i) * ES);
+#pragma unroll
+          for (int v = 0; v < NV; ++v) {
+            const u32x4 w = src[v];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              if (BF16) {
+                const double e0 = __uint_as_float(w[q] << 16), e1 = __uint_as_float(w[q] & 0xFFFF0000u);
+                sx = fma(e0, e0, sx);
+                sx = fma(e1, e1, sx);
+              } else {
+                const double e = __uint_as_float(w[q]);
+                sx = fma(e, e, sx);
+              }
+            }
+          }
+        }
+        sx = wave_sum_d(sx);
+        const double inv64 = 1.0 / (sqrt((double)H) * (sqrt(sx) + OQ_EPS));
         const int g0 = lane & ~(BL - 1);   // first lane of this lane's block group
         // the gather addresses again (not kept live through the transform)
         uint32_t raddr[16];
@@ -772,10 +812,14 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
           part = group_sum<BL>(part);
           if (gm && lane == L) {
             const double u = part * inv64;
-            // u is exact here: its cell holds the only threshold that can lie in it
+            // u is exact to fp64 rounding; its cell holds the only threshold near it
             const double cf = fmin(fmax(floor((u - a.g_lo) * a.g_invw), 0.0), (double)(G - 1));
             const int2 e = lut[(int)cf];
-            const uint32_t nidx = (uint32_t)e.y + ((double)__int_as_float(e.x) < u ? 1u : 0u);
+            // against the fp64 threshold (thr + thr_lo), not its fp32 rounding
+            const double th = e.x == __float_as_int(INFINITY)
+                                  ? (double)INFINITY
+                                  : (double)__int_as_float(e.x) + (double)a.thr_lo[e.y];
+            const uint32_t nidx = (uint32_t)e.y + (th < u ? 1u : 0u);
             pw.set(r, nidx);
             flags &= ~(1u << r);
           }

@@ -145,9 +145,10 @@ oq_status oq_quantize_weights(const void* W, oq_dtype w_dtype, int32_t d_out, in
  * x_idx = #{j : thresholds[j] < x_rot / (s + OQ_EPS)}.  Hot path.
  *
  * The rotation runs in fp32.  A coordinate whose fp32 value lies within a
- * certified rounding bound of a decision threshold is recomputed in fp64
- * before its index is chosen, so indices equal those of an exact rotation
- * except within ~1e-6 relative of a threshold.
+ * certified rounding bound of a decision threshold is recomputed in fp64 and
+ * compared with the fp64 threshold before its index is chosen, so every index
+ * is the one exact arithmetic gives, up to fp64 rounding (coordinates within
+ * ~1e-12 relative of a threshold).
  *
  * x          : dev [T][d], fp32 or bf16 (x_dtype), row-major.
  * T          : tokens, >= 0 (int64).   d: h | d, and d/16 either a multiple of 64

@@ -15,7 +15,11 @@ from oracle import codebook, quant, rpbh
 REL_XROT = 1e-5       # per-token relative L2 of the rotated activations
 REL_S = 1e-5          # relative error of the token norms
 REL_GEMM = 2e-3       # relative Frobenius error of the GEMM output
-BAND = 1e-6           # indices may differ only within BAND * |theta| of a threshold
+# Indices may differ only within BAND * |theta| of a threshold: the kernels
+# decide every coordinate as exact arithmetic would (certified fp32 fast path,
+# fp64 recheck against the fp64 threshold), so what is left is the fp64
+# rounding of the two sides' different summation orders (< ~1e-12 relative).
+BAND = 1e-11
 
 
 def log(msg):

@@ -1,8 +1,8 @@
 """GPU parity: liboq's kernels against the fp64 oracle on the same seeded
 inputs, through the C ABI (Python binding = marshalling only).
 
-Bars: packed indices bit-exact except within 1e-6 |theta| of a threshold
-(weights: bit-exact); rotated activations and norms within 1e-5 relative;
+Bars: packed indices bit-exact except within 1e-11 |theta| of a threshold
+(fp64 summation order; weights: bit-exact); rotated activations and norms within 1e-5 relative;
 GEMM within 2e-3 relative Frobenius of the oracle's dequantized product of
 the GPU's own indices, norms and scales."""
 
