@@ -85,6 +85,15 @@ struct QlArgs {
   int32_t epilogue;
   uint16_t tab_a[256];   // fp16 bits of sqrt(K) * c_a
   uint16_t tab_w[256];   // fp16 bits of sqrt(K) * c_w
+  // Work split (set by ql_launch): tiles [0, n_dp) are whole-tile work; the
+  // last sk_tiles tiles are split by K stages over workgroups 0 .. sk_ranks-1
+  // (stream-K), which exchange fp32 partial tiles through ws (one 256 x 256
+  // slot per workgroup) and flags (one word per workgroup, zero between launches).
+  int64_t n_dp;
+  int32_t sk_tiles;
+  int32_t sk_ranks;
+  float* ws;
+  uint32_t* flags;
 };
 hipError_t ql_launch(const QlArgs& a, int bits_a, int bits_w, hipStream_t stream);
 

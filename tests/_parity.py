@@ -67,6 +67,27 @@ def index_mismatches(gpu_idx: np.ndarray, ora_idx: np.ndarray, u: np.ndarray, th
     return n, inband, n - inband
 
 
+def tile_rel_max(y, ref, rows, tile: int = 256):
+    """Largest relative Frobenius error over the kernel's 256 x 256 output tiles
+    (restricted to the checked rows), so that one wrong tile cannot hide in the
+    total."""
+    y = np.asarray(y, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    rb = np.asarray(rows) // tile
+    worst = 0.0
+    for b in np.unique(rb):
+        sel = rb == b
+        for c0 in range(0, ref.shape[1], tile):
+            r = ref[sel, c0:c0 + tile]
+            den = np.linalg.norm(r)
+            num = np.linalg.norm(y[sel, c0:c0 + tile] - r)
+            if den > 0:
+                worst = max(worst, float(num / den))
+            elif num > 0:
+                worst = float("inf")
+    return worst
+
+
 def rel_frob(a, b):
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
@@ -160,6 +181,6 @@ def check_gemm(x_idx, s, w_idx, w_norm, d: int, bits_a: int, bits_w: int, bias=N
     yg = y.cpu().numpy()[rows]
     err = rel_frob(yg, ref)
     rep = {"name": name, "T": T, "N": w_norm.shape[0], "K": d, "checked_rows": len(rows), "rel_frob": err,
-           "finite": bool(np.all(np.isfinite(yg)))}
+           "tile_rel_max": tile_rel_max(yg, ref, rows), "finite": bool(np.all(np.isfinite(yg)))}
     log(f"[gemm] {rep}")
     return y, rep

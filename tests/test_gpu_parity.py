@@ -40,6 +40,7 @@ def _assert_w(rep):
 def _assert_gemm(rep):
     assert rep["finite"], rep
     assert rep["rel_frob"] <= P.REL_GEMM, rep
+    assert rep["tile_rel_max"] <= P.REL_GEMM, rep
 
 
 def run_linear(lin, index=0, T=None, seed=0, bias=False, act_rows=None, gemm_rows=None, x=None, W_=None,
@@ -192,6 +193,42 @@ def test_gemm_repeatable():
     y1, _ = P.check_gemm(x_idx, s, w_idx, w_norm, lin.d_in, 4, 4)
     y2, _ = P.check_gemm(x_idx, s, w_idx, w_norm, lin.d_in, 4, 4)
     assert torch.equal(y1, y2)
+
+
+# ---- stream-K: the last, partial round of tiles split by K stages -----------------
+
+
+def _gemm_twice(lin, rows, seed):
+    """The GEMM on two scale vectors in a row, every tile of both checked: the
+    second launch must not consume the first one's partial tiles."""
+    x, Wm = synth.gen_linear(lin, seed, 0)
+    x_idx, s, ra = P.check_activations(x, lin.act_dtype, lin.h, lin.bits_a, rows=np.arange(min(8, lin.T)),
+                                       want_x_rot=False, name=lin.name)
+    _assert_act(ra)
+    w_idx, w_norm, rw = P.check_weights(Wm, lin.h, lin.bits_w, name=lin.name)
+    _assert_w(rw)
+    for k, scale in enumerate((1.0, 1.75)):
+        sk = s * scale
+        _, rg = P.check_gemm(x_idx, sk, w_idx, w_norm, lin.d_in, lin.bits_a, lin.bits_w, rows=rows,
+                             name=f"{lin.name}-launch{k}")
+        _assert_gemm(rg)
+
+
+@pytest.mark.parametrize("T,d,d_out,bits_w,bits_a", [(1024, 3072, 3072, 4, 8), (1024, 12288, 3072, 4, 8),
+                                                     (300, 512, 300, 4, 4), (1000, 1024, 2000, 2, 4)])
+def test_stream_k_split_tiles(T, d, d_out, bits_w, bits_a):
+    # fewer tiles than 70 % of the CUs: every tile is split by K stages over
+    # 2-5 workgroups (stream-K)
+    lin = synth.Linear(f"sk-{T}x{d}x{d_out}", T, d, d_out, 256, bits_w, bits_a, "student_t", "bf16", 10, 30.0,
+                       0.5, 5, 10.0)
+    _gemm_twice(lin, np.arange(T), seed=T + d)
+
+
+def test_flux_qkv_last_round_tiles_twice():
+    # 648 tiles on 256 CUs: the last, partial round (M rows 3072 .. 4607 in the
+    # grouped raster order) checked tile by tile, on two launches in a row
+    lin = W["flux_qkv_w4a4"].linears[0]
+    _gemm_twice(lin, np.arange(3072, lin.T), seed=5)
 
 
 # ---- full sizes, sampled outputs ------------------------------------------------
