@@ -86,12 +86,13 @@ struct QlArgs {
   uint16_t tab_a[256];   // fp16 bits of sqrt(K) * c_a
   uint16_t tab_w[256];   // fp16 bits of sqrt(K) * c_w
   // Work split (set by ql_launch): tiles [0, n_dp) are whole-tile work; the
-  // last sk_tiles tiles are split by K stages over workgroups 0 .. sk_ranks-1
-  // (stream-K), which exchange fp32 partial tiles through ws (one 256 x 256
-  // slot per workgroup) and flags (one word per workgroup, zero between launches).
+  // last sk_tiles tiles are split by K stages (stream-K, XCD by XCD, runs of
+  // at least sk_lmin stages); workgroups exchange fp32 partial tiles through ws
+  // (one 256 x 256 slot per workgroup) and flags (one word per workgroup, zero
+  // between launches).
   int64_t n_dp;
   int32_t sk_tiles;
-  int32_t sk_ranks;
+  int32_t sk_lmin;
   float* ws;
   uint32_t* flags;
 };

@@ -180,15 +180,17 @@ oq_status oq_rotate_quantize_act(const void* x, oq_dtype x_dtype, int64_t T, int
  * MFMA operands with fp32 accumulation; the epilogue scales by
  * s * w_norm / d_in.  Hot path.
  *
- * Problems with fewer 256 x 256 output tiles than 70 % of the device's CUs
- * are split by K (stream-K): workgroups exchange fp32 partial tiles through a
- * workspace that the library owns, one per (device, stream): cus * 256 KB of
- * uncached device memory plus cus flags, allocated on the first such launch
- * on that stream and kept until the process ends (at most 16 streams per
- * device; past that, or while the stream is being captured into a graph and
- * has no workspace yet, the launch runs whole tiles).  The partial tiles are
- * added in a fixed order, so results are deterministic; launches that share
- * a stream are ordered by it.
+ * The last, partial round of 256 x 256 output tiles (all tiles, when there
+ * are fewer than the device's CUs) is split by K (stream-K) when it holds at
+ * least 8 tiles and would leave more than a fifth of the CUs idle: the
+ * workgroups of each XCD exchange fp32 partial tiles through a workspace that
+ * the library owns, one per (device, stream): cus * 256 KB plus cus flags,
+ * allocated on the first such launch on that stream and kept until the
+ * process ends (at most 16 streams per device; past that, while the stream is
+ * being captured into a graph and has no workspace yet, or on a device whose
+ * workgroups are not dealt round-robin over 8 XCDs, the launch runs whole
+ * tiles).  The partial tiles are added in a fixed order, so results are
+ * deterministic; launches that share a stream are ordered by it.
  *
  * x_idx       : dev [T][d_in * bits_a / 8], from oq_rotate_quantize_act.
  * s           : dev [T] float.

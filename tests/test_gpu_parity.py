@@ -215,18 +215,19 @@ def _gemm_twice(lin, rows, seed):
 
 
 @pytest.mark.parametrize("T,d,d_out,bits_w,bits_a", [(1024, 3072, 3072, 4, 8), (1024, 12288, 3072, 4, 8),
-                                                     (300, 512, 300, 4, 4), (1000, 1024, 2000, 2, 4)])
+                                                     (2100, 1024, 300, 4, 4), (1000, 1024, 2000, 2, 4)])
 def test_stream_k_split_tiles(T, d, d_out, bits_w, bits_a):
-    # fewer tiles than 70 % of the CUs: every tile is split by K stages over
-    # 2-5 workgroups (stream-K)
+    # fewer tiles than CUs (18 to 48, some ragged): every tile is split by K
+    # stages over 2-5 workgroups of one XCD (stream-K)
     lin = synth.Linear(f"sk-{T}x{d}x{d_out}", T, d, d_out, 256, bits_w, bits_a, "student_t", "bf16", 10, 30.0,
                        0.5, 5, 10.0)
     _gemm_twice(lin, np.arange(T), seed=T + d)
 
 
 def test_flux_qkv_last_round_tiles_twice():
-    # 648 tiles on 256 CUs: the last, partial round (M rows 3072 .. 4607 in the
-    # grouped raster order) checked tile by tile, on two launches in a row
+    # 648 tiles on 256 CUs: two whole rounds, then the last 136 tiles (M rows
+    # 3072 .. 4607 in the grouped raster order) split by K stages, 17 per XCD;
+    # checked tile by tile, on two launches in a row
     lin = W["flux_qkv_w4a4"].linears[0]
     _gemm_twice(lin, np.arange(3072, lin.T), seed=5)
 
