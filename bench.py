@@ -35,7 +35,7 @@ FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, TFLOP/s
 # bench (FETCH_SIZE x 2, WRITE_SIZE x 1: the copy-kernel calibration), valid only
 # for the kernel source they were taken on (sha256 prefix); otherwise null.
 MEASURED_TRAFFIC = {
-    "free_bit_quantization_amd/csrc/qlinear.hip": ("13875ee6448514a5", 125.8e6, 169.9e6),
+    "free_bit_quantization_amd/csrc/qlinear.hip": ("4174002d10553c64", 176.7e6, 232.8e6),
     "free_bit_quantization_amd/csrc/rotate_quantize.hip": ("1feb412e40dc2196", 28.9e6, 7.2e6),
 }
 
@@ -294,7 +294,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(ql_tflops, 2), "peak": FP16_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(ql_tflops / FP16_MFMA_PEAK_TFLOPS, 4),
                      "traffic": traffic_of("free_bit_quantization_amd/csrc/qlinear.hip"), "traffic_unit": "bytes",
-                     "kernel": "oq_qlinear (ql_kernel<4,4,false>: whole tiles)", "algorithmic": f"2*T*K*N = {flops:.4g} flop"},
+                     "kernel": "oq_qlinear (ql_kernel<4,4,true>: 2 whole-tile rounds + stream-K last round)", "algorithmic": f"2*T*K*N = {flops:.4g} flop"},
         "roofline_rotate_quant": {"bound": "hbm", "achieved": round(rq_gbs, 1), "peak": HBM_PEAK_GBS,
                                   "unit": "GB/s", "frac": round(rq_gbs / HBM_PEAK_GBS, 4),
                                   "traffic": traffic_of("free_bit_quantization_amd/csrc/rotate_quantize.hip"),
