@@ -194,12 +194,14 @@ oq_status oq_rotate_quantize_act(const void* x, oq_dtype x_dtype, int64_t T, int
 
 oq_status oq_qlinear(const uint8_t* x_idx, const float* s, int64_t T, const uint8_t* w_idx, const float* w_norm,
                      int32_t d_out, int32_t d_in, const double* centroids_a, int32_t bits_a,
-                     const double* centroids_w, int32_t bits_w, const float* bias, int32_t epilogue, float* y,
+                     const double* centroids_w, int32_t bits_w, const float* bias, int32_t epilogue, void* y,
                      hipStream_t stream) {
   if (T < 0 || d_out < 0) return fail(OQ_EINVAL, "T and d_out must be >= 0");
   if (d_in <= 0) return fail(OQ_EINVAL, "d_in must be > 0");
   if (!bits_ok(bits_a) || !bits_ok(bits_w)) return fail(OQ_EINVAL, "bits must be 2, 3, 4, 6 or 8");
-  if (epilogue != OQ_EPI_NONE && epilogue != OQ_EPI_GELU_ERF) return fail(OQ_EINVAL, "unknown epilogue %d", epilogue);
+  if ((epilogue & ~(0xFF | OQ_EPI_OUT_BF16)) != 0 ||
+      ((epilogue & 0xFF) != OQ_EPI_NONE && (epilogue & 0xFF) != OQ_EPI_GELU_ERF))
+    return fail(OQ_EINVAL, "unknown epilogue %d", epilogue);
   if (!centroids_a || !centroids_w) return fail(OQ_EINVAL, "centroids is NULL");
   const int La = 1 << bits_a, Lw = 1 << bits_w;
   for (int i = 0; i < La; ++i)

@@ -80,9 +80,9 @@ struct QlArgs {
   int32_t N;
   int32_t K;
   const float* bias;
-  float* y;
+  void* y;               // float, or bf16 bits with OQ_EPI_OUT_BF16
   float scale;           // 1 / K (tables hold sqrt(K) * c)
-  int32_t epilogue;
+  int32_t epilogue;      // OQ_EPI_NONE / OQ_EPI_GELU_ERF, | OQ_EPI_OUT_BF16
   uint16_t tab_a[256];   // fp16 bits of sqrt(K) * c_a
   uint16_t tab_w[256];   // fp16 bits of sqrt(K) * c_w
   // Work split (set by ql_launch): tiles [0, n_dp) are whole-tile work; the

@@ -139,14 +139,17 @@ struct Pack16 {
     if constexpr (NW > 2) w[2] = (uint32_t)hi;
     if constexpr (NW > 3) w[3] = (uint32_t)(hi >> 32);
   }
-  // p: first byte of the slot (2 BITS bytes; aligned to 2 BITS bytes' natural unit)
+  // p: first byte of the slot (2 BITS bytes; aligned to 2 BITS bytes' natural
+  // unit).  Non-temporal: the indices are read by the next kernel, not this one
+  // (2 % faster than plain stores on the FLUX QKV rows).
   __device__ __forceinline__ void store(uint8_t* p) const {
     if constexpr (BITS == 2) {
-      *reinterpret_cast<uint32_t*>(p) = w[0];
+      __builtin_nontemporal_store(w[0], reinterpret_cast<uint32_t*>(p));
     } else if constexpr (BITS == 4) {
-      *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+      typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+      __builtin_nontemporal_store(u32x2_t{w[0], w[1]}, reinterpret_cast<u32x2_t*>(p));
     } else if constexpr (BITS == 8) {
-      *reinterpret_cast<u32x4*>(p) = u32x4{w[0], w[1], w[2], w[3]};
+      __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4*>(p));
     } else if constexpr (BITS == 6) {   // 12 bytes, 4-byte aligned
       uint32_t* q = reinterpret_cast<uint32_t*>(p);
       q[0] = w[0]; q[1] = w[1]; q[2] = w[2];

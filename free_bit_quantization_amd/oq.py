@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "liboq.so")
 
 OQ_OK, OQ_EINVAL, OQ_EUNSUPPORTED, OQ_ENOCONV, OQ_EDEVICE = 0, -1, -2, -3, -4
 OQ_F32, OQ_BF16, OQ_F16 = 0, 1, 2
-OQ_EPI_NONE, OQ_EPI_GELU_ERF = 0, 1
+OQ_EPI_NONE, OQ_EPI_GELU_ERF, OQ_EPI_OUT_BF16 = 0, 1, 0x100
 
 # every symbol include/oq.h declares
 EXPORTS = ("oq_last_error", "oq_version", "oq_build_rpbh", "oq_build_block_rht", "oq_lloyd_max",
@@ -188,19 +188,24 @@ def oq_rotate_quantize_act(x, h: int, perm, sign, thresholds, bits_a: int, x_idx
 
 
 def oq_qlinear(x_idx, s, w_idx, w_norm, d_in: int, centroids_a, bits_a: int, centroids_w, bits_w: int,
-               bias=None, epilogue: int = OQ_EPI_NONE, y=None, stream=None):
-    """Codebook GEMM: returns y f32[T, d_out]."""
+               bias=None, epilogue: int = OQ_EPI_NONE, y=None, stream=None, out_dtype=None):
+    """Codebook GEMM: returns y[T, d_out], float32 (default) or bfloat16
+    (out_dtype=torch.bfloat16, or a bf16 y: the fp32 result rounded to nearest even)."""
     import torch
     T = s.shape[0]
     d_out = w_norm.shape[0]
     if y is None:
-        y = torch.empty((T, d_out), dtype=torch.float32, device=s.device)
+        y = torch.empty((T, d_out), dtype=out_dtype or torch.float32, device=s.device)
+    if y.dtype == torch.bfloat16:
+        epilogue |= OQ_EPI_OUT_BF16
+    elif y.dtype != torch.float32:
+        raise TypeError("y must be float32 or bfloat16")
     ca, cap = _host_f64(centroids_a)
     cw, cwp = _host_f64(centroids_w)
     _check(lib().oq_qlinear(_dev(x_idx, torch.uint8), _dev(s, torch.float32), T, _dev(w_idx, torch.uint8),
                             _dev(w_norm, torch.float32), d_out, d_in, cap, bits_a, cwp, bits_w,
                             _dev(bias, torch.float32) if bias is not None else None, epilogue,
-                            _dev(y, torch.float32), _stream(stream)))
+                            _dev(y, y.dtype), _stream(stream)))
     return y
 
 

@@ -56,7 +56,7 @@ enum {
 };
 
 typedef enum { OQ_F32 = 0, OQ_BF16 = 1, OQ_F16 = 2 } oq_dtype;
-enum { OQ_EPI_NONE = 0, OQ_EPI_GELU_ERF = 1 };
+enum { OQ_EPI_NONE = 0, OQ_EPI_GELU_ERF = 1, OQ_EPI_OUT_BF16 = 0x100 };
 
 /* eps added to the activation norm (and to weight row norms) before the
  * division; the pages use an eps without giving its value. */
@@ -204,8 +204,9 @@ oq_status oq_rotate_quantize_act(const void* x, oq_dtype x_dtype, int64_t T, int
  *               other widths the pages name, W3A4, W2A3, W6A6.  3- and 6-bit
  *               indices are widened to 4 and 8 bits as they are staged.
  * bias        : dev [d_out] float or NULL.
- * epilogue    : OQ_EPI_NONE or OQ_EPI_GELU_ERF.
- * y           : dev [T][d_out] float, written.
+ * epilogue    : OQ_EPI_NONE or OQ_EPI_GELU_ERF, optionally | OQ_EPI_OUT_BF16.
+ * y           : dev [T][d_out], written: float, or bf16 (the fp32 result
+ *               rounded to nearest even) with OQ_EPI_OUT_BF16.
  * x_idx, w_idx, w_norm, bias and y must be 16-byte aligned (OQ_EINVAL otherwise).
  * Errors      : OQ_EINVAL, OQ_EUNSUPPORTED, OQ_EDEVICE.
  */
@@ -213,7 +214,7 @@ oq_status oq_qlinear(const uint8_t* x_idx, const float* s, int64_t T,
                      const uint8_t* w_idx, const float* w_norm, int32_t d_out, int32_t d_in,
                      const double* centroids_a, int32_t bits_a,
                      const double* centroids_w, int32_t bits_w,
-                     const float* bias, int32_t epilogue, float* y, hipStream_t stream);
+                     const float* bias, int32_t epilogue, void* y, hipStream_t stream);
 
 /*
  * oq_quantize_weights_int4 -- INT4 round-to-nearest, weight only, for the

@@ -232,6 +232,31 @@ def test_flux_qkv_last_round_tiles_twice():
     _gemm_twice(lin, np.arange(3072, lin.T), seed=5)
 
 
+# ---- bf16 output: the fp32 result rounded to nearest even, bit for bit -----------
+
+
+@pytest.mark.parametrize("T,d,d_out,bits_w,bits_a,gelu", [(300, 1024, 258, 4, 4, True),    # per-element stores
+                                                          (520, 3072, 1024, 2, 4, False),  # row stores
+                                                          (1024, 3072, 3072, 4, 8, True)])  # stream-K split
+def test_gemm_bf16_output_is_rounded_fp32(T, d, d_out, bits_w, bits_a, gelu):
+    from free_bit_quantization_amd import oq
+    lin = synth.Linear(f"bf16out-{T}", T, d, d_out, 256, bits_w, bits_a, "student_t", "bf16", 10, 30.0, 0.5, 5,
+                       10.0)
+    x, Wm = synth.gen_linear(lin, 7, 0)
+    x_idx, s, _ = P.check_activations(x, "bf16", lin.h, bits_a, rows=np.arange(4), want_x_rot=False)
+    w_idx, w_norm, _ = P.check_weights(Wm, lin.h, bits_w)
+    ca = P.library_codebook(d, bits_a)
+    cw = P.library_codebook(d, bits_w)
+    bias = torch.from_numpy(synth.gen_bias(d_out, 2)).cuda()
+    epi = oq.OQ_EPI_GELU_ERF if gelu else oq.OQ_EPI_NONE
+    y32 = oq.oq_qlinear(x_idx, s, w_idx, w_norm, d, ca.c, bits_a, cw.c, bits_w, bias=bias, epilogue=epi)
+    y16 = oq.oq_qlinear(x_idx, s, w_idx, w_norm, d, ca.c, bits_a, cw.c, bits_w, bias=bias, epilogue=epi,
+                        out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert y16.dtype == torch.bfloat16
+    assert torch.equal(y16.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16))
+
+
 # ---- full sizes, sampled outputs ------------------------------------------------
 
 

@@ -116,6 +116,11 @@ def test_device_calls_reject_bad_arguments_without_launching():
     cp, c2p = c.ctypes.data, c2.ctypes.data
     assert L.oq_qlinear(f, f, 4, f, f, 8, 256, cp, 4, cp, 5, None, 0, f, None) == oq.OQ_EINVAL
     assert L.oq_qlinear(f, f, 4, f, f, 8, 256, cp, 4, cp, 4, None, 5, f, None) == oq.OQ_EINVAL
+    # the bf16-output flag combines with either activation, nothing else does
+    assert L.oq_qlinear(f, f, 4, f, f, 8, 256, cp, 4, cp, 4, None, 0x200, f, None) == oq.OQ_EINVAL
+    assert L.oq_qlinear(f, f, 4, f, f, 8, 256, cp, 4, cp, 4, None, oq.OQ_EPI_OUT_BF16 | 2, f, None) == oq.OQ_EINVAL
+    assert L.oq_qlinear(f, f, 0, f, f, 8, 256, cp, 4, cp, 4, None, oq.OQ_EPI_OUT_BF16 | oq.OQ_EPI_GELU_ERF, f,
+                        None) == oq.OQ_OK
     assert L.oq_qlinear(f, f, 4, f, f, 8, 256, None, 4, cp, 4, None, 0, f, None) == oq.OQ_EINVAL
     assert L.oq_qlinear(None, f, 4, f, f, 8, 256, cp, 4, cp, 4, None, 0, f, None) == oq.OQ_EINVAL
     assert L.oq_qlinear(f, f, 4, f, f, 8, 96, cp, 4, cp, 4, None, 0, f, None) == oq.OQ_EUNSUPPORTED
