@@ -198,7 +198,7 @@ def test_gemm_repeatable():
 # ---- stream-K: the last, partial round of tiles split by K stages -----------------
 
 
-def _gemm_twice(lin, rows, seed):
+def _gemm_twice(lin, rows, seed, bias=False, gelu=False):
     """The GEMM on two scale vectors in a row, every tile of both checked: the
     second launch must not consume the first one's partial tiles."""
     x, Wm = synth.gen_linear(lin, seed, 0)
@@ -207,10 +207,11 @@ def _gemm_twice(lin, rows, seed):
     _assert_act(ra)
     w_idx, w_norm, rw = P.check_weights(Wm, lin.h, lin.bits_w, name=lin.name)
     _assert_w(rw)
+    b = synth.gen_bias(lin.d_out, seed) if bias else None
     for k, scale in enumerate((1.0, 1.75)):
         sk = s * scale
-        _, rg = P.check_gemm(x_idx, sk, w_idx, w_norm, lin.d_in, lin.bits_a, lin.bits_w, rows=rows,
-                             name=f"{lin.name}-launch{k}")
+        _, rg = P.check_gemm(x_idx, sk, w_idx, w_norm, lin.d_in, lin.bits_a, lin.bits_w, bias=b, gelu=gelu,
+                             rows=rows, name=f"{lin.name}-launch{k}")
         _assert_gemm(rg)
 
 
@@ -218,10 +219,12 @@ def _gemm_twice(lin, rows, seed):
                                                      (2100, 1024, 300, 4, 4), (1000, 1024, 2000, 2, 4)])
 def test_stream_k_split_tiles(T, d, d_out, bits_w, bits_a):
     # fewer tiles than CUs (18 to 48, some ragged): every tile is split by K
-    # stages over 2-5 workgroups of one XCD (stream-K)
+    # stages over 2-5 workgroups of one XCD (stream-K); bias and GELU on the
+    # ragged shape (the finisher applies them after summing the partials)
     lin = synth.Linear(f"sk-{T}x{d}x{d_out}", T, d, d_out, 256, bits_w, bits_a, "student_t", "bf16", 10, 30.0,
                        0.5, 5, 10.0)
-    _gemm_twice(lin, np.arange(T), seed=T + d)
+    ragged = d_out % 256 != 0
+    _gemm_twice(lin, np.arange(T), seed=T + d, bias=ragged, gelu=ragged)
 
 
 def test_flux_qkv_last_round_tiles_twice():
