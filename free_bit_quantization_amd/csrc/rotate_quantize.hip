@@ -663,6 +663,7 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
     wave_sync_lds();  // the staged row is visible to every lane
 
     const uint32_t rowbase = (uint32_t)(Ly.wave0 + (size_t)wave * Ly.wave_bytes);
+    double inv64 = 0.0;   // 1 / (sqrt(h) (s + eps)) from the exact norm, once a slot needs it
 #pragma unroll
     for (int j = 0; j < J; ++j) {
       // ---- 2. gather ---------------------------------------------------------------
@@ -759,29 +760,32 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
           }
         }
         // the norm again, exactly: fp64 squares of the staged row (sign flips do
-        // not change them); the fast path's fp32 partials are only certified
-        double sx = 0.0;
+        // not change them); the fast path's fp32 partials are only certified.
+        // Once per token (8-bit codebooks flag ~2 coordinates per token).
+        if (inv64 == 0.0) {
+          double sx = 0.0;
 #pragma unroll
-        for (int i = 0; i < J; ++i) {
-          const u32x4* src = reinterpret_cast<const u32x4*>(wrow + (size_t)16 * (lane + 64 * i) * ES);
+          for (int i = 0; i < J; ++i) {
+            const u32x4* src = reinterpret_cast<const u32x4*>(wrow + (size_t)16 * (lane + 64 * i) * ES);
 #pragma unroll
-          for (int v = 0; v < NV; ++v) {
-            const u32x4 w = src[v];
+            for (int v = 0; v < NV; ++v) {
+              const u32x4 w = src[v];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              if (BF16) {
-                const double e0 = __uint_as_float(w[q] << 16), e1 = __uint_as_float(w[q] & 0xFFFF0000u);
-                sx = fma(e0, e0, sx);
-                sx = fma(e1, e1, sx);
-              } else {
-                const double e = __uint_as_float(w[q]);
-                sx = fma(e, e, sx);
+              for (int q = 0; q < 4; ++q) {
+                if (BF16) {
+                  const double e0 = __uint_as_float(w[q] << 16), e1 = __uint_as_float(w[q] & 0xFFFF0000u);
+                  sx = fma(e0, e0, sx);
+                  sx = fma(e1, e1, sx);
+                } else {
+                  const double e = __uint_as_float(w[q]);
+                  sx = fma(e, e, sx);
+                }
               }
             }
           }
+          sx = wave_sum_d(sx);
+          inv64 = 1.0 / (sqrt((double)H) * (sqrt(sx) + OQ_EPS));
         }
-        sx = wave_sum_d(sx);
-        const double inv64 = 1.0 / (sqrt((double)H) * (sqrt(sx) + OQ_EPS));
         const int g0 = lane & ~(BL - 1);   // first lane of this lane's block group
         // the gather addresses again (not kept live through the transform)
         uint32_t raddr[16];
