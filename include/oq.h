@@ -189,8 +189,10 @@ oq_status oq_rotate_quantize_act(const void* x, oq_dtype x_dtype, int64_t T, int
  * process ends (at most 16 streams per device; past that, while the stream is
  * being captured into a graph and has no workspace yet, or on a device whose
  * workgroups are not dealt round-robin over 8 XCDs, the launch runs whole
- * tiles).  The partial tiles are added in a fixed order, so results are
- * deterministic; launches that share a stream are ordered by it.
+ * tiles).  The first such launch on a device also runs a small probe kernel
+ * of the XCD dispatch and synchronises its stream once.  The partial tiles
+ * are added in a fixed order, so results are deterministic; launches that
+ * share a stream are ordered by it.
  *
  * x_idx       : dev [T][d_in * bits_a / 8], from oq_rotate_quantize_act.
  * s           : dev [T] float.
