@@ -216,7 +216,10 @@ def _gemm_twice(lin, rows, seed, bias=False, gelu=False):
 
 
 @pytest.mark.parametrize("T,d,d_out,bits_w,bits_a", [(1024, 3072, 3072, 4, 8), (1024, 12288, 3072, 4, 8),
-                                                     (2100, 1024, 300, 4, 4), (1000, 1024, 2000, 2, 4)])
+                                                     (2100, 1024, 300, 4, 4), (1000, 1024, 2000, 2, 4),
+                                                     (512, 1024, 1024, 4, 4),    # 8 tiles: one per XCD, 4 pieces
+                                                     (2048, 512, 1024, 4, 4),    # 4 K stages per tile
+                                                     (1024, 1024, 1024, 6, 6)])  # 6-bit widths (128 x 64 blocks)
 def test_stream_k_split_tiles(T, d, d_out, bits_w, bits_a):
     # fewer tiles than CUs (18 to 48, some ragged): every tile is split by K
     # stages over 2-5 workgroups of one XCD (stream-K); bias and GELU on the
