@@ -13,7 +13,8 @@ Prints one JSON line.  Per-kernel durations come from HIP events recorded
 on the launch stream around every kernel of the timed steps.  With --sweep it
 prints one line per linear of every workload instead (throughput and roofline
 fractions only); with --modulation one line per AdaLN modulation projection
-(the INT4 round-to-nearest W4A16 kernel, HBM roofline).
+(the INT4 round-to-nearest W4A16 kernel, HBM roofline); with --mlp the
+chained MLP pair, once with an fp32 and once with a bf16 hidden state.
 """
 
 from __future__ import annotations
@@ -153,6 +154,76 @@ def measure_linear(lin, index, steps, warmup, ring_mb, dev):
     return r
 
 
+def measure_mlp(up, down, hidden, steps, warmup, ring_mb, dev):
+    """Time the chained MLP pair: rotate-quantize x, up GEMM with the GELU
+    epilogue into the hidden state h, rotate-quantize h, down GEMM.  h is
+    fp32 or bf16 (the up GEMM rounds its output to nearest even)."""
+    import torch
+    from free_bit_quantization_amd import oq, synth
+
+    T, K, H, N, hb = up.T, up.d_in, up.d_out, down.d_out, up.h
+    assert down.d_in == H and down.T == T
+    x, W_up = synth.gen_linear(up, 0, 0)
+    _, W_dn = synth.gen_linear(down, 0, 1, T=1, need_act=False)
+    rot = {}
+    for d in (K, H):
+        pm, sg = oq.oq_build_rpbh(d, hb, 0)
+        rot[d] = (torch.from_numpy(pm).to(dev), torch.from_numpy(sg).to(dev))
+    cb = {(d, b): oq.oq_lloyd_max(d, b) for d in (K, H) for b in {up.bits_a, up.bits_w, down.bits_a, down.bits_w}}
+    wq = []
+    for lin, Wm in ((up, W_up), (down, W_dn)):
+        Wd = torch.from_numpy(Wm).to(dev)
+        wq.append(oq.oq_quantize_weights(Wd, hb, *rot[lin.d_in], cb[(lin.d_in, lin.bits_w)][1], lin.bits_w))
+        del Wd
+    xt = torch.from_numpy(x).to(dev).to(torch.bfloat16)
+    nring = max(1, math.ceil(ring_mb * 1e6 / (xt.numel() * xt.element_size())))
+    ring = [xt] + [torch.roll(xt, shifts=i * 7, dims=0).contiguous() for i in range(1, nring)]
+    hd = torch.bfloat16 if hidden == "bf16" else torch.float32
+    xi_u = torch.empty((T, K * up.bits_a // 8), dtype=torch.uint8, device=dev)
+    s_u = torch.empty(T, dtype=torch.float32, device=dev)
+    hbuf = torch.empty((T, H), dtype=hd, device=dev)
+    xi_d = torch.empty((T, H * down.bits_a // 8), dtype=torch.uint8, device=dev)
+    s_d = torch.empty(T, dtype=torch.float32, device=dev)
+    y = torch.empty((T, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def kernels(i):
+        yield lambda: oq.oq_rotate_quantize_act(ring[i % nring], hb, *rot[K], cb[(K, up.bits_a)][1], up.bits_a,
+                                                x_idx=xi_u, s=s_u, stream=stream)
+        yield lambda: oq.oq_qlinear(xi_u, s_u, wq[0][0], wq[0][1], K, cb[(K, up.bits_a)][0], up.bits_a,
+                                    cb[(K, up.bits_w)][0], up.bits_w, epilogue=oq.OQ_EPI_GELU_ERF, y=hbuf,
+                                    stream=stream)
+        yield lambda: oq.oq_rotate_quantize_act(hbuf, hb, *rot[H], cb[(H, down.bits_a)][1], down.bits_a,
+                                                x_idx=xi_d, s=s_d, stream=stream)
+        yield lambda: oq.oq_qlinear(xi_d, s_d, wq[1][0], wq[1][1], H, cb[(H, down.bits_a)][0], down.bits_a,
+                                    cb[(H, down.bits_w)][0], down.bits_w, y=y, stream=stream)
+
+    for i in range(warmup):
+        for k in kernels(i):
+            k()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        ev[i][0].record(stream)
+        for j, k in enumerate(kernels(i)):
+            k()
+            ev[i][j + 1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / steps
+    per = [sum(e[j].elapsed_time(e[j + 1]) for e in ev) / steps for j in range(4)]
+    flops = 2.0 * T * K * H + 2.0 * T * H * N
+    return {"workload": "flux_mlp_chain", "hidden": hidden, "tokens": T, "d_in": K, "d_hidden": H, "d_out": N,
+            "bits_w": up.bits_w, "bits_a": up.bits_a, "h": hb, "hidden_bytes": T * H * hbuf.element_size(),
+            "ms_per_step": round(ms_step, 5), "tokens_per_s": round(T / (ms_step * 1e-3), 1),
+            "TFLOPs": round(flops / (ms_step * 1e-3) / 1e12, 2),
+            "rq_up_ms": round(per[0], 5), "gemm_up_ms": round(per[1], 5), "rq_down_ms": round(per[2], 5),
+            "gemm_down_ms": round(per[3], 5), "activation_ring_buffers": nring}
+
+
 def measure_modulation(lin, steps, warmup, ring_mb, dev):
     """Time the W4A16 modulation projection (INT4 RTN weights streamed from HBM).
 
@@ -220,6 +291,9 @@ def main():
                     help="one line per linear of every workload (tokens/s, GB/s, TFLOP/s, roofline fractions)")
     ap.add_argument("--modulation", action="store_true",
                     help="one line per AdaLN modulation projection (INT4 RTN W4A16 kernel)")
+    ap.add_argument("--mlp", action="store_true",
+                    help="the chained FLUX-like MLP pair (rq, up GEMM + GELU, rq, down GEMM), one line with an "
+                         "fp32 and one with a bf16 hidden state")
     ap.add_argument("--sweep-workloads", default="",
                     help="comma-separated workload names for --sweep (default: all)")
     args = ap.parse_args()
@@ -240,6 +314,13 @@ def main():
             for lin in lins:
                 r = measure_modulation(lin, max(args.steps, 50), args.warmup, args.ring_mb, dev)
                 print(json.dumps(modulation_line(name, lin, r)), flush=True)
+        return
+
+    if args.mlp:
+        up, down = synth.workloads()["flux_mlp_w2a4"].linears
+        for hidden in ("f32", "bf16"):
+            print(json.dumps(measure_mlp(up, down, hidden, args.steps, args.warmup, args.ring_mb, dev)), flush=True)
+            torch.cuda.empty_cache()
         return
 
     if args.sweep:

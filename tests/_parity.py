@@ -163,8 +163,12 @@ def check_weights(W: np.ndarray, h: int, bits: int, seed: int = 0, name: str = "
 
 
 def check_gemm(x_idx, s, w_idx, w_norm, d: int, bits_a: int, bits_w: int, bias=None, gelu=False,
-               rows: Optional[np.ndarray] = None, name: str = ""):
-    """GEMM on the GPU vs the oracle's dequantized product of the GPU's own indices."""
+               rows: Optional[np.ndarray] = None, name: str = "", out_dtype=None):
+    """GEMM on the GPU vs the oracle's dequantized product of the GPU's own indices.
+
+    With out_dtype=torch.bfloat16 the GEMM also runs with bf16 output; that
+    tensor must hold the fp32 output rounded to nearest even, bit for bit
+    (report key "bf16_equal"), and it is the one returned."""
     import torch
     ca = library_codebook(d, bits_a)
     cw = library_codebook(d, bits_w)
@@ -182,5 +186,11 @@ def check_gemm(x_idx, s, w_idx, w_norm, d: int, bits_a: int, bits_w: int, bias=N
     err = rel_frob(yg, ref)
     rep = {"name": name, "T": T, "N": w_norm.shape[0], "K": d, "checked_rows": len(rows), "rel_frob": err,
            "tile_rel_max": tile_rel_max(yg, ref, rows), "finite": bool(np.all(np.isfinite(yg)))}
+    if out_dtype is not None:
+        y16 = oq.oq_qlinear(x_idx, s, w_idx, w_norm, d, ca.c, bits_a, cw.c, bits_w, bias=bd,
+                            epilogue=oq.OQ_EPI_GELU_ERF if gelu else oq.OQ_EPI_NONE, out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        rep["bf16_equal"] = bool(torch.equal(y16.view(torch.int16), y.to(out_dtype).view(torch.int16)))
+        y = y16
     log(f"[gemm] {rep}")
     return y, rep

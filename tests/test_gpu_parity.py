@@ -44,7 +44,7 @@ def _assert_gemm(rep):
 
 
 def run_linear(lin, index=0, T=None, seed=0, bias=False, act_rows=None, gemm_rows=None, x=None, W_=None,
-               x_dtype=None, kind="rpbh"):
+               x_dtype=None, kind="rpbh", out_dtype=None):
     P.log(f"== linear {lin.name} T={T or lin.T} K={lin.d_in} N={lin.d_out} W{lin.bits_w}A{lin.bits_a}")
     xg, Wg = synth.gen_linear(lin, seed, index, T=T, need_act=x is None)
     x = xg if x is None else x
@@ -56,8 +56,10 @@ def run_linear(lin, index=0, T=None, seed=0, bias=False, act_rows=None, gemm_row
     _assert_w(rw)
     b = synth.gen_bias(lin.d_out, seed) if bias else None
     y, rg = P.check_gemm(x_idx, s, w_idx, w_norm, lin.d_in, lin.bits_a, lin.bits_w, bias=b,
-                         gelu=lin.epilogue == "gelu", rows=gemm_rows, name=lin.name)
+                         gelu=lin.epilogue == "gelu", rows=gemm_rows, name=lin.name, out_dtype=out_dtype)
     _assert_gemm(rg)
+    if out_dtype is not None:
+        assert rg["bf16_equal"], rg
     return y
 
 
@@ -83,6 +85,16 @@ def test_flux_mlp_chain_prefix():
     x_down = y_up.cpu().numpy().astype(np.float32)
     _, W_down = synth.gen_linear(down, 0, 1, T=1, need_act=False)
     run_linear(down, index=1, T=264, x=x_down, W_=W_down, x_dtype="f32")
+
+
+def test_flux_mlp_chain_prefix_bf16_hidden():
+    # the hidden state kept in bf16: the up GEMM writes GELU(y) rounded to
+    # bf16 and the down rotate-quantize reads that tensor as it is
+    up, down = W["flux_mlp_w2a4"].linears
+    h16 = run_linear(up, index=0, T=264, out_dtype=torch.bfloat16)
+    x_down = h16.float().cpu().numpy()
+    _, W_down = synth.gen_linear(down, 0, 1, T=1, need_act=False)
+    run_linear(down, index=1, T=264, x=x_down, W_=W_down, x_dtype="bf16")
 
 
 def test_wan_ffn_prefix_ragged():
@@ -286,6 +298,16 @@ def test_full_flux_mlp_w2a4_chain():
     x_down = y_up.cpu().numpy()
     _, W_down = synth.gen_linear(down, 0, 1, T=1, need_act=False)
     run_linear(down, index=1, x=x_down, W_=W_down, x_dtype="f32", act_rows=_sample_rows(down.T, 512),
+               gemm_rows=rows)
+
+
+def test_full_flux_mlp_w2a4_chain_bf16_hidden():
+    up, down = W["flux_mlp_w2a4"].linears
+    rows = _sample_rows(up.T, 64)
+    h16 = run_linear(up, index=0, act_rows=_sample_rows(up.T, 256), gemm_rows=rows, out_dtype=torch.bfloat16)
+    x_down = h16.float().cpu().numpy()
+    _, W_down = synth.gen_linear(down, 0, 1, T=1, need_act=False)
+    run_linear(down, index=1, x=x_down, W_=W_down, x_dtype="bf16", act_rows=_sample_rows(down.T, 256),
                gemm_rows=rows)
 
 
