@@ -22,7 +22,8 @@
 //      hold at most one threshold, so idx = base[cell] + (u > theta[cell]),
 //      decided by the sign of one fma;
 //   5. guard: a coordinate whose fp32 value lies within a certified rounding
-//      bound of its threshold is recomputed in fp64 by the wavefront (rare)
+//      bound of its threshold is recomputed in fp64 by the lanes holding its
+//      Hadamard block (rare; the groups of a wavefront work side by side)
 //      and compared with the fp64 threshold (fp32 value + fp32 residual)
 //      before its index is set, so every index is the one exact arithmetic
 //      gives, up to fp64 rounding.  Bound: each output of the m = log2 h
@@ -139,6 +140,23 @@ struct Pack16 {
     if constexpr (NW > 2) w[2] = (uint32_t)hi;
     if constexpr (NW > 3) w[3] = (uint32_t)(hi >> 32);
   }
+  // index r (any r)
+  __device__ __forceinline__ uint32_t get(int r) const {
+    uint64_t lo = w[0], hi = 0;
+    if constexpr (NW > 1) lo |= (uint64_t)w[1] << 32;
+    if constexpr (NW > 2) hi = w[2];
+    if constexpr (NW > 3) hi |= (uint64_t)w[3] << 32;
+    const uint64_t m = (1ull << BITS) - 1;
+    const int pos = BITS * r;
+    uint64_t v;
+    if (pos < 64) {
+      v = lo >> pos;
+      if (pos + BITS > 64) v |= hi << (64 - pos);
+    } else {
+      v = hi >> (pos - 64);
+    }
+    return (uint32_t)(v & m);
+  }
   // p: first byte of the slot (2 BITS bytes; aligned to 2 BITS bytes' natural
   // unit).  Non-temporal: the indices are read by the next kernel, not this one
   // (2 % faster than plain stores on the FLUX QKV rows).
@@ -189,12 +207,14 @@ __device__ __forceinline__ int count_below_f64(const float* thr, int n, double u
 }
 
 // #{j : theta_j < u} against the fp64 thresholds theta_j = thr[j] + thr_lo[j]
-// (the sum is exact in fp64: thr_lo lies below half an fp32 ulp of thr)
-__device__ __forceinline__ int count_below_exact(const float* thr, const float* thr_lo, int n, double u) {
-  int lo = 0;
-#pragma unroll
-  for (int step = 128; step >= 1; step >>= 1)
-    if (lo + step <= n && (double)thr[lo + step - 1] + (double)thr_lo[lo + step - 1] < u) lo += step;
+// (the sum is exact in fp64: thr_lo lies below half an fp32 ulp of thr),
+// walking from a guess (the fast path's index, at most a step or two away):
+// the result is exact for any guess in [0, n], since the thresholds ascend
+// strictly.
+__device__ __forceinline__ int count_below_exact_from(const float* thr, const float* thr_lo, int n, double u,
+                                                      int lo) {
+  while (lo > 0 && (double)thr[lo - 1] + (double)thr_lo[lo - 1] >= u) --lo;
+  while (lo < n && (double)thr[lo] + (double)thr_lo[lo] < u) ++lo;
   return lo;
 }
 
@@ -439,20 +459,28 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
     }
     if (!valid) flags = 0;
 
-    // fp64 recheck of guarded coordinates, by the whole wavefront
+    // fp64 recheck of guarded coordinates.  An output of Hadamard block b
+    // depends only on that block's inputs, which the GS lanes of the block
+    // hold (an aligned group: GS = BL with two passes, 1 with one), so each
+    // group rechecks its own lowest flagged output per round and the groups
+    // of a wavefront run their rounds side by side.  The group sum adds the
+    // same nonzero parts in the same order as a wavefront sum would.
+    constexpr int GS = TWO_PASS ? BL : 1;
+    static_assert(GS <= 16, "group sums span at most 16 lanes");
     while (true) {
       const uint64_t bal = __ballot(flags != 0);
       if (bal == 0) break;
-      const int L = __ffsll((unsigned long long)bal) - 1;
+      const int g0 = lane & ~(GS - 1);
+      const uint32_t gbits = (uint32_t)(bal >> g0) & ((1u << GS) - 1u);
+      const int L = gbits ? g0 + __ffs(gbits) - 1 : lane;   // this group's leader
       const uint32_t fl = __shfl(flags, L);
-      const int r = __ffs(fl) - 1;
       const int slL = __shfl(sl, L);
-      const int tlL = __shfl(tl, L);
+      const int r = fl ? __ffs(fl) - 1 : 0;
       const int gi = 16 * slL + r;
       const int b = gi >> LOG2H;
       const int j = gi & (H - 1);
       double part = 0.0;
-      if (tl == tlL) {
+      if (gbits) {
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
           const int gk = gin(rr);
@@ -465,10 +493,10 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
           }
         }
       }
-      part = wave_sum_d(part);
-      if (lane == L) {
+      if constexpr (GS > 1) part = group_sum<GS>(part);
+      if (gbits && lane == L) {
         const double u = part / (sqrt((double)H) * (s64 + OQ_EPS));
-        pk.set(r, (uint32_t)count_below_exact(thr, a.thr_lo, nthr, u));
+        pk.set(r, (uint32_t)count_below_exact_from(thr, a.thr_lo, nthr, u, (int)pk.get(r)));
         flags &= ~(1u << r);
       }
     }
