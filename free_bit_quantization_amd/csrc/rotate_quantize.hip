@@ -188,7 +188,7 @@ __host__ __device__ inline RqLayout rq_layout(int d, int log2h, int es, int tpw,
   const int h = 1 << log2h;
   L.lut = 0;
   L.thr = align16(8 * (size_t)(G > 0 ? G : 1));
-  L.row = L.thr + 256 * 4;
+  L.row = L.thr + 2 * 256 * 4;   // thr, then thr_lo
   L.row_stride = align16((size_t)tpw * d * es);
   L.trans = L.row + 2 * L.row_stride;
   const size_t trans_bytes = log2h > 4 ? (size_t)tpw * (d / h) * (h + kPad) * 4 : 0;
@@ -244,7 +244,12 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
   double* red = reinterpret_cast<double*>(smem + Ly.red);
 
   // ---- thresholds and the search grid --------------------------------------
-  for (int i = tid; i < 256; i += blockDim.x) thr[i] = i < nthr ? a.thr[i] : INFINITY;
+  // thresholds (fp32) and their fp64 residuals side by side: the recheck reads
+  // both with per-lane indices, which LDS serves without a memory round trip
+  for (int i = tid; i < 256; i += blockDim.x) {
+    thr[i] = i < nthr ? a.thr[i] : INFINITY;
+    thr[256 + i] = i < nthr ? a.thr_lo[i] : 0.f;
+  }
   __syncthreads();
   if (G > 0) {
     const double w = 1.0 / a.g_invw;
@@ -496,7 +501,7 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
       if constexpr (GS > 1) part = group_sum<GS>(part);
       if (gbits && lane == L) {
         const double u = part / (sqrt((double)H) * (s64 + OQ_EPS));
-        pk.set(r, (uint32_t)count_below_exact_from(thr, a.thr_lo, nthr, u, (int)pk.get(r)));
+        pk.set(r, (uint32_t)count_below_exact_from(thr, thr + 256, nthr, u, (int)pk.get(r)));
         flags &= ~(1u << r);
       }
     }
@@ -534,8 +539,8 @@ struct RqwLayout {
 __host__ __device__ inline RqwLayout rqw_layout(int d, int log2h, int es, int G, int wpb) {
   RqwLayout L;
   const int h = 1 << log2h;
-  L.thr = 0;
-  L.lut = 256 * 4;
+  L.thr = 0;              // thr, then thr_lo
+  L.lut = 2 * 256 * 4;
   L.mtab = L.lut + align16(8 * (size_t)(G > 0 ? G : 1));
   const size_t mwords = es == 2 ? (size_t)d / 2 : (size_t)d;   // sign masks of the source words
   L.atab = L.mtab + align16(4 * mwords);                          // gather offsets, 4 d bytes
@@ -616,7 +621,10 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
   if (gw < T) fetch(gw);
   __builtin_amdgcn_sched_barrier(0);
 
-  for (int i = tid; i < 256; i += blockDim.x) thr[i] = i < nthr ? a.thr[i] : INFINITY;
+  for (int i = tid; i < 256; i += blockDim.x) {
+    thr[i] = i < nthr ? a.thr[i] : INFINITY;
+    thr[256 + i] = i < nthr ? a.thr_lo[i] : 0.f;   // fp64 residuals, read by the recheck
+  }
   int8_t* sp = reinterpret_cast<int8_t*>(smem + Ly.wave0);   // sign' scratch over the wave buffers
   uint32_t* atab = reinterpret_cast<uint32_t*>(smem + Ly.atab);
 #pragma unroll
@@ -853,7 +861,7 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
             // against the fp64 threshold (thr + thr_lo), not its fp32 rounding
             const double th = e.x == __float_as_int(INFINITY)
                                   ? (double)INFINITY
-                                  : (double)__int_as_float(e.x) + (double)a.thr_lo[e.y];
+                                  : (double)__int_as_float(e.x) + (double)thr[256 + e.y];
             const uint32_t nidx = (uint32_t)e.y + (th < u ? 1u : 0u);
             pw.set(r, nidx);
             flags &= ~(1u << r);
