@@ -298,7 +298,7 @@ def main():
                     help="comma-separated workload names for --sweep (default: all)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (the layer is "
+        print("bench.py measures one GPU only: the library has no multi-GPU path (the layer is "
               "token-parallel; see the sharding design notes). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
