@@ -192,7 +192,11 @@ oq_status oq_rotate_quantize_act(const void* x, oq_dtype x_dtype, int64_t T, int
  * tiles).  The first such launch on a device also runs a small probe kernel
  * of the XCD dispatch and synchronises its stream once.  The partial tiles
  * are added in a fixed order, so results are deterministic; launches that
- * share a stream are ordered by it.
+ * share a stream are ordered by it.  A graph captured on a stream that
+ * already has a workspace records that workspace: replay it only ordered
+ * with the other launches that use it (on the capture stream, or after them);
+ * two split launches that overlap on one workspace race, and the tiles whose
+ * exchange fails come out as NaN.
  *
  * x_idx       : dev [T][d_in * bits_a / 8], from oq_rotate_quantize_act.
  * s           : dev [T] float.
