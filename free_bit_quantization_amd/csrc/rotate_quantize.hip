@@ -30,9 +30,10 @@
 //      butterfly stages is a depth-m tree of +-sums of exact inputs, so its
 //      error is at most gamma_m L1(block), gamma_m = m u / (1 - m u), u = 2^-24;
 //      the guard uses (m + 1) u L1 / (sqrt(h) s) with L1 and s as computed
-//      (their relative errors fit in the extra u), plus k u max|theta| for the
-//      scale c = 1 / (sqrt(h) (s + eps)) and theta's rounding to fp32 (u), at
-//      |u| ~ |theta|: k = 6 where s comes from fp64 sums of the exact squares
+//      (their relative errors fit in the extra u), plus k u |theta| of the
+//      threshold compared, for the scale c = 1 / (sqrt(h) (s + eps)) and
+//      theta's rounding to fp32 (u), at |u| ~ |theta| (the second-order k u
+//      times the radius fits in the butterflies' spare u L1): k = 6 where s comes from fp64 sums of the exact squares
 //      (c rounded once from fp64), k = 4 J + 5 where the fast path sums 8 J
 //      squares per lane in fp32 ((8 J + 1) u in s^2, (4 J + 3.5) u in c); the
 //      recheck then takes s from fp64 squares of the staged row;
@@ -656,7 +657,6 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
   }
   __syncthreads();  // tables complete, sign scratch consumed
 
-  const float thmax = nthr > 0 ? fmaxf(fabsf(thr[0]), fabsf(thr[nthr - 1])) : 0.f;
   const float inv_sqrt_h = (float)(1.0 / sqrt((double)H));
   const float kSqrtH = (float)sqrt((double)H);
   const float og = (float)(-a.g_lo * a.g_invw);
@@ -760,9 +760,9 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
       l1 = group_sum<BL>(l1);
 
       // ---- 4./5. grid search and guard --------------------------------------------
-      const float rad = fmaf(thmax, kRel, kGam * l1 * c);
+      const float radb = kGam * l1 * c;
       Pack16<BITS> pw;
-      bool near = false;
+      uint32_t flags = 0;
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         int2 e[8];
@@ -774,10 +774,11 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
           const int r = 8 * hf + q;
-          const float dd = fmaf(y[r], c, -__int_as_float(e[q].x));
+          const float th = __int_as_float(e[q].x);
+          const float dd = fmaf(y[r], c, -th);
           const uint32_t idx = (uint32_t)e[q].y + (dd > 0.f ? 1u : 0u);
           pw.put(r, idx);
-          near |= fabsf(dd) < rad;
+          flags |= (fabsf(dd) < fmaf(fabsf(th), kRel, radb) ? 1u : 0u) << r;
         }
       }
 
@@ -785,16 +786,7 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
       // block hold its inputs (pass 1) and its outputs (pass 2), so each group
       // of BL lanes recomputes one of its flagged coordinates per round, all
       // groups at once, with an fp64 sum over the group.
-      if (__ballot(near) != 0) {
-        uint32_t flags = 0;
-        if (near) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int ci = (int)__builtin_amdgcn_fmed3f(fmaf(y[r], cg, og), 0.0f, (float)(G - 1));
-            const bool nr = fabsf(fmaf(y[r], c, -__int_as_float(lut[ci].x))) < rad;
-            flags |= (nr ? 1u : 0u) << r;
-          }
-        }
+      if (__ballot(flags != 0) != 0) {
         // the norm again, exactly: fp64 squares of the staged row (sign flips do
         // not change them); the fast path's fp32 partials are only certified.
         // Once per token (8-bit codebooks flag ~2 coordinates per token).
