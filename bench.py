@@ -36,7 +36,7 @@ FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, TFLOP/s
 # bench (FETCH_SIZE x 2, WRITE_SIZE x 1: the copy-kernel calibration), valid only
 # for the kernel source they were taken on (sha256 prefix); otherwise null.
 MEASURED_TRAFFIC = {
-    "free_bit_quantization_amd/csrc/qlinear.hip": ("e07daf64fd648f74", 178.4e6, 233.9e6),
+    "free_bit_quantization_amd/csrc/qlinear.hip": ("e07daf64fd648f74", 178.3e6, 233.9e6),
     "free_bit_quantization_amd/csrc/rotate_quantize.hip": ("4ab491b3ee839feb", 28.9e6, 7.2e6),
 }
 
