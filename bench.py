@@ -3,7 +3,8 @@
 
 One step = the whole hot path on one batch: rotate-and-quantize of the
 token activations (oq_rotate_quantize_act) followed by the codebook GEMM
-(oq_qlinear), on the FLUX.1-like double-stream QKV linear (4608 tokens,
+(oq_qlinear_splitk with a workspace allocated before timing; --whole-tiles:
+oq_qlinear), on the FLUX.1-like double-stream QKV linear (4608 tokens,
 3072 -> 9216, W4A4, h = 256).  Weights are quantized once, offline,
 before timing.  Inputs are resident in HBM when the timed region starts;
 the activation batches rotate through a ring of buffers larger than the
@@ -39,6 +40,10 @@ MEASURED_TRAFFIC = {
     "free_bit_quantization_amd/csrc/qlinear.hip": ("e07daf64fd648f74", 178.3e6, 233.9e6),
     "free_bit_quantization_amd/csrc/rotate_quantize.hip": ("4ab491b3ee839feb", 28.9e6, 7.2e6),
 }
+
+
+TRAFFIC_SOURCE = ("rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE of this bench, profiles/flux_qkv_w4a4_kernels.md "
+                  "(null when the kernel source changed since)")
 
 
 def traffic_of(src: str):
@@ -85,8 +90,10 @@ def cpu_baseline(lin, x, Wm, perm, sign, c_a, th_a, c_w, th_w, target_s: float =
             "tokens_per_s": n * reps / t}
 
 
-def measure_linear(lin, index, steps, warmup, ring_mb, dev):
-    """Time rotate-quantize + codebook GEMM of one linear (inputs resident in HBM)."""
+def measure_linear(lin, index, steps, warmup, ring_mb, dev, split=True):
+    """Time rotate-quantize + codebook GEMM of one linear (inputs resident in HBM).
+    split: the GEMM through oq_qlinear_splitk with a workspace allocated before
+    timing (stream-K tail where the shape takes it), else oq_qlinear."""
     import torch
     from free_bit_quantization_amd import oq, synth
 
@@ -112,11 +119,19 @@ def measure_linear(lin, index, steps, warmup, ring_mb, dev):
     y = torch.empty((T, N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream()
     epi = oq.OQ_EPI_GELU_ERF if lin.epilogue == "gelu" else oq.OQ_EPI_NONE
+    ws = oq.qlinear_workspace(T, N, K, lin.bits_a, lin.bits_w) if split else None
+
+    def gemm():
+        if split:
+            oq.oq_qlinear_splitk(x_idx, s, w_idx, w_norm, K, c_a, lin.bits_a, c_w, lin.bits_w, ws, epilogue=epi, y=y,
+                                 stream=stream)
+        else:
+            oq.oq_qlinear(x_idx, s, w_idx, w_norm, K, c_a, lin.bits_a, c_w, lin.bits_w, epilogue=epi, y=y,
+                          stream=stream)
 
     def step(i):
         oq.oq_rotate_quantize_act(ring[i % nring], h, pd, sd, th_a, lin.bits_a, x_idx=x_idx, s=s, stream=stream)
-        oq.oq_qlinear(x_idx, s, w_idx, w_norm, K, c_a, lin.bits_a, c_w, lin.bits_w, epilogue=epi, y=y,
-                      stream=stream)
+        gemm()
 
     for i in range(warmup):
         step(i)
@@ -133,8 +148,7 @@ def measure_linear(lin, index, steps, warmup, ring_mb, dev):
         e[0].record(stream)
         oq.oq_rotate_quantize_act(ring[i % nring], h, pd, sd, th_a, lin.bits_a, x_idx=x_idx, s=s, stream=stream)
         e[1].record(stream)
-        oq.oq_qlinear(x_idx, s, w_idx, w_norm, K, c_a, lin.bits_a, c_w, lin.bits_w, epilogue=epi, y=y,
-                      stream=stream)
+        gemm()
         e[2].record(stream)
     end.record(stream)
     torch.cuda.synchronize()
@@ -150,6 +164,7 @@ def measure_linear(lin, index, steps, warmup, ring_mb, dev):
     r = dict(T=T, K=K, N=N, h=h, es=es, nring=nring, ms_step=ms_step, t_rq=t_rq, t_ql=t_ql, t_wall=t_wall,
              rq_bytes=rq_bytes, flops=flops, rq_gbs=rq_bytes / (t_rq * 1e-3) / 1e9,
              ql_tflops=flops / (t_ql * 1e-3) / 1e12, value=flops / (ms_step * 1e-3) / 1e12,
+             entry="oq_qlinear_splitk" if ws is not None else "oq_qlinear", ws_bytes=0 if ws is None else ws.numel(),
              inputs=(x, Wm, perm, sign, c_a, th_a, c_w, th_w))
     return r
 
@@ -296,6 +311,8 @@ def main():
                          "fp32 and one with a bf16 hidden state")
     ap.add_argument("--sweep-workloads", default="",
                     help="comma-separated workload names for --sweep (default: all)")
+    ap.add_argument("--whole-tiles", action="store_true",
+                    help="time the GEMM through oq_qlinear (whole tiles, no workspace) instead of oq_qlinear_splitk")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path (the layer is "
@@ -327,12 +344,13 @@ def main():
         names = [n for n in args.sweep_workloads.split(",") if n] or synth.WORKLOAD_ORDER
         for name in names:
             for k, lin in enumerate(synth.workloads()[name].linears):
-                r = measure_linear(lin, k, args.steps, args.warmup, args.ring_mb, dev)
+                r = measure_linear(lin, k, args.steps, args.warmup, args.ring_mb, dev, split=not args.whole_tiles)
                 print(json.dumps({
                     "workload": name, "linear": lin.name, "tokens": r["T"], "d_in": r["K"], "d_out": r["N"],
                     "h": r["h"], "bits_w": lin.bits_w, "bits_a": lin.bits_a, "act_dtype": lin.act_dtype,
                     "epilogue": lin.epilogue, "tokens_per_s": round(r["T"] / (r["ms_step"] * 1e-3), 1),
                     "ms_per_step": round(r["ms_step"], 5),
+                    "qlinear_entry": r["entry"],
                     "qlinear_TFLOPs": round(r["ql_tflops"], 2), "qlinear_ms": round(r["t_ql"], 5),
                     "qlinear_frac_fp16_peak": round(r["ql_tflops"] / FP16_MFMA_PEAK_TFLOPS, 4),
                     "rotate_quant_GBps": round(r["rq_gbs"], 1), "rotate_quant_ms": round(r["t_rq"], 5),
@@ -343,7 +361,7 @@ def main():
 
     wl = synth.workloads()[args.workload]
     lin = wl.linears[0]
-    r = measure_linear(lin, 0, args.steps, args.warmup, args.ring_mb, dev)
+    r = measure_linear(lin, 0, args.steps, args.warmup, args.ring_mb, dev, split=not args.whole_tiles)
     T, K, N, h = r["T"], r["K"], r["N"], r["h"]
     es, rq_bytes, flops = r["es"], r["rq_bytes"], r["flops"]
     ms_step, t_rq, t_ql = r["ms_step"], r["t_rq"], r["t_ql"]
@@ -375,11 +393,15 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(ql_tflops, 2), "peak": FP16_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(ql_tflops / FP16_MFMA_PEAK_TFLOPS, 4),
                      "traffic": traffic_of("free_bit_quantization_amd/csrc/qlinear.hip"), "traffic_unit": "bytes",
-                     "kernel": "oq_qlinear (ql_kernel<4,4,true>: 2 whole-tile rounds + stream-K last round)", "algorithmic": f"2*T*K*N = {flops:.4g} flop"},
+                     "traffic_source": TRAFFIC_SOURCE,
+                     "kernel": (f"{r['entry']} (ql_kernel<{lin.bits_a},{lin.bits_w},"
+                                + ("true>: whole-tile rounds + stream-K last round)" if r["ws_bytes"] else
+                                   "false>: whole tiles)")),
+                     "workspace_bytes": r["ws_bytes"], "algorithmic": f"2*T*K*N = {flops:.4g} flop"},
         "roofline_rotate_quant": {"bound": "hbm", "achieved": round(rq_gbs, 1), "peak": HBM_PEAK_GBS,
                                   "unit": "GB/s", "frac": round(rq_gbs / HBM_PEAK_GBS, 4),
                                   "traffic": traffic_of("free_bit_quantization_amd/csrc/rotate_quantize.hip"),
-                                  "traffic_unit": "bytes",
+                                  "traffic_unit": "bytes", "traffic_source": TRAFFIC_SOURCE,
                                   "kernel": "oq_rotate_quantize_act (rq_wave_kernel<8,bf16,4,3>)",
                                   "algorithmic": f"T*(K*{es} + K*{lin.bits_a}/8 + 4) = {rq_bytes} B"},
         "wall_s_timed": round(t_wall, 4),

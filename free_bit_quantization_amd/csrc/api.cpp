@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "oq_internal.h"
@@ -51,6 +52,13 @@ oq_status check_thresholds(const double* th, int n, bool need_f32) {
   return OQ_OK;
 }
 
+// (bits_w, bits_a) pairs with a GEMM kernel: W4A4, W2A4, W4A8, W2A8 and the
+// other widths the pages name, W3A4, W2A3, W6A6
+bool gemm_widths_ok(int bits_a, int bits_w) {
+  return (bits_a == 4 && (bits_w == 2 || bits_w == 3 || bits_w == 4)) || (bits_a == 8 && (bits_w == 2 || bits_w == 4)) ||
+         (bits_a == 3 && bits_w == 2) || (bits_a == 6 && bits_w == 6);
+}
+
 uint16_t to_f16_bits(double v) {
   const _Float16 h = (_Float16)v;
   uint16_t b;
@@ -88,8 +96,16 @@ oq_status oq_lloyd_max(int32_t d, int32_t bits, double* centroids, double* thres
   if (d < 3) return fail(OQ_EINVAL, "d must be >= 3 (got %d)", d);
   if (bits < 1 || bits > 8) return fail(OQ_EINVAL, "bits must be in 1..8 (got %d)", bits);
   if (!centroids || !thresholds) return fail(OQ_EINVAL, "centroids / thresholds is NULL");
+  // The Newton step cap can be lowered through the environment, so that the
+  // non-convergence path can be exercised (OQ_LLOYD_MAX_NEWTON_STEPS = n >= 0).
+  int max_newton = oq::kLloydMaxNewton;
+  if (const char* env = std::getenv("OQ_LLOYD_MAX_NEWTON_STEPS")) {
+    char* end = nullptr;
+    const long v = std::strtol(env, &end, 10);
+    if (end != env && *end == 0 && v >= 0 && v < max_newton) max_newton = (int)v;
+  }
   double resid = 0.0;
-  if (oq::lloyd_max_fd(d, bits, centroids, thresholds, mse, &resid) != 0)
+  if (oq::lloyd_max_fd(d, bits, max_newton, centroids, thresholds, mse, &resid) != 0)
     return fail(OQ_ENOCONV, "Lloyd-Max residual %.3g above 1e-10 (d=%d, bits=%d)", resid, d, bits);
   return ok();
 }
@@ -192,10 +208,16 @@ oq_status oq_rotate_quantize_act(const void* x, oq_dtype x_dtype, int64_t T, int
   return ok();
 }
 
-oq_status oq_qlinear(const uint8_t* x_idx, const float* s, int64_t T, const uint8_t* w_idx, const float* w_norm,
-                     int32_t d_out, int32_t d_in, const double* centroids_a, int32_t bits_a,
-                     const double* centroids_w, int32_t bits_w, const float* bias, int32_t epilogue, void* y,
-                     hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the GEMM entry points; fills everything of a but the
+// work split.  Returns OQ_OK with *nothing = true for an empty product.
+oq_status qlinear_args(const uint8_t* x_idx, const float* s, int64_t T, const uint8_t* w_idx, const float* w_norm,
+                       int32_t d_out, int32_t d_in, const double* centroids_a, int32_t bits_a,
+                       const double* centroids_w, int32_t bits_w, const float* bias, int32_t epilogue, void* y,
+                       oq::QlArgs* a, bool* nothing) {
   if (T < 0 || d_out < 0) return fail(OQ_EINVAL, "T and d_out must be >= 0");
   if (d_in <= 0) return fail(OQ_EINVAL, "d_in must be > 0");
   if (!bits_ok(bits_a) || !bits_ok(bits_w)) return fail(OQ_EINVAL, "bits must be 2, 3, 4, 6 or 8");
@@ -212,28 +234,112 @@ oq_status oq_qlinear(const uint8_t* x_idx, const float* s, int64_t T, const uint
   auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; };
   if (misaligned(x_idx) || misaligned(w_idx) || misaligned(w_norm) || misaligned(y) || misaligned(bias))
     return fail(OQ_EINVAL, "x_idx, w_idx, w_norm, bias and y must be 16-byte aligned");
-  const bool has_kernel = (bits_a == 4 && (bits_w == 2 || bits_w == 3 || bits_w == 4)) ||
-                          (bits_a == 8 && (bits_w == 2 || bits_w == 4)) || (bits_a == 3 && bits_w == 2) ||
-                          (bits_a == 6 && bits_w == 6);
-  if (!has_kernel) return fail(OQ_EUNSUPPORTED, "no GEMM kernel for W%dA%d", bits_w, bits_a);
-  const int kstage = (bits_a == 8 || bits_a == 6) ? 64 : 128;  // K indices per pipeline stage of the GEMM
+  if (!gemm_widths_ok(bits_a, bits_w)) return fail(OQ_EUNSUPPORTED, "no GEMM kernel for W%dA%d", bits_w, bits_a);
+  const int kstage = oq::ql_stage_k(bits_a);
   if (d_in % kstage != 0) return fail(OQ_EUNSUPPORTED, "d_in must be a multiple of %d for A%d (got %d)", kstage, bits_a, d_in);
   const double sk = std::sqrt((double)d_in);
   for (int i = 0; i < La; ++i)
     if (std::fabs(sk * centroids_a[i]) > 60000.0) return fail(OQ_EINVAL, "sqrt(d_in)*centroids_a exceeds fp16");
   for (int i = 0; i < Lw; ++i)
     if (std::fabs(sk * centroids_w[i]) > 60000.0) return fail(OQ_EINVAL, "sqrt(d_in)*centroids_w exceeds fp16");
-  if (T == 0 || d_out == 0) return ok();
+  *nothing = T == 0 || d_out == 0;
+  *a = oq::QlArgs{};
+  a->x_idx = x_idx; a->s = s; a->T = T; a->w_idx = w_idx; a->w_norm = w_norm;
+  a->N = d_out; a->K = d_in; a->bias = bias; a->y = y; a->epilogue = epilogue;
+  a->scale = (float)(1.0 / d_in);
+  for (int i = 0; i < 256; ++i) a->tab_a[i] = i < La ? to_f16_bits(sk * centroids_a[i]) : 0;
+  for (int i = 0; i < 256; ++i) a->tab_w[i] = i < Lw ? to_f16_bits(sk * centroids_w[i]) : 0;
+  return OQ_OK;
+}
 
-  oq::QlArgs a{};
-  a.x_idx = x_idx; a.s = s; a.T = T; a.w_idx = w_idx; a.w_norm = w_norm;
-  a.N = d_out; a.K = d_in; a.bias = bias; a.y = y; a.epilogue = epilogue;
-  a.scale = (float)(1.0 / d_in);
-  for (int i = 0; i < 256; ++i) a.tab_a[i] = i < La ? to_f16_bits(sk * centroids_a[i]) : 0;
-  for (int i = 0; i < 256; ++i) a.tab_w[i] = i < Lw ? to_f16_bits(sk * centroids_w[i]) : 0;
+// Compute units of the current device.
+oq_status device_cus(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return device_error(e, "hipGetDevice");
+  e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return device_error(e, "hipDeviceGetAttribute");
+  if (*cus <= 0) return fail(OQ_EDEVICE, "device reports %d compute units", *cus);
+  return OQ_OK;
+}
+
+oq::QlSplit qlinear_plan(int64_t T, int32_t d_out, int32_t d_in, int32_t bits_a, int cus, int64_t slots) {
+  const int64_t ntiles = ((T + 255) / 256) * (((int64_t)d_out + 255) / 256);
+  return oq::ql_split_plan(ntiles, d_in / oq::ql_stage_k(bits_a), cus, slots);
+}
+
+// Launch with a workspace of `slots` partial-tile slots laid out at ws (ws may
+// be NULL with slots = 0: whole tiles only).
+oq_status qlinear_launch(oq::QlArgs& a, int32_t bits_a, int32_t bits_w, int cus, unsigned char* ws, int64_t slots,
+                         hipStream_t stream) {
+  a.sp = qlinear_plan(a.T, a.N, a.K, bits_a, cus, slots);
+  if (a.sp.sk_tiles > 0) {
+    a.hdr = reinterpret_cast<uint32_t*>(ws);
+    a.flags = reinterpret_cast<uint32_t*>(ws + oq::ql_ws_flags_offset());
+    a.slots = reinterpret_cast<float*>(ws + oq::ql_ws_slots_offset(slots));
+  }
   hipError_t e = oq::ql_launch(a, bits_a, bits_w, stream);
   if (e != hipSuccess) return device_error(e, "oq_qlinear launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+oq_status oq_qlinear(const uint8_t* x_idx, const float* s, int64_t T, const uint8_t* w_idx, const float* w_norm,
+                     int32_t d_out, int32_t d_in, const double* centroids_a, int32_t bits_a,
+                     const double* centroids_w, int32_t bits_w, const float* bias, int32_t epilogue, void* y,
+                     hipStream_t stream) {
+  oq::QlArgs a;
+  bool nothing = false;
+  oq_status st = qlinear_args(x_idx, s, T, w_idx, w_norm, d_out, d_in, centroids_a, bits_a, centroids_w, bits_w,
+                              bias, epilogue, y, &a, &nothing);
+  if (st != OQ_OK) return st;
+  if (nothing) return ok();
+  int cus = 0;
+  if ((st = device_cus(&cus)) != OQ_OK) return st;
+  return qlinear_launch(a, bits_a, bits_w, cus, nullptr, 0, stream);
+}
+
+oq_status oq_qlinear_workspace_size(int64_t T, int32_t d_out, int32_t d_in, int32_t bits_a, int32_t bits_w,
+                                    size_t* bytes) {
+  if (!bytes) return fail(OQ_EINVAL, "bytes is NULL");
+  if (T < 0 || d_out < 0 || d_in <= 0) return fail(OQ_EINVAL, "need T >= 0, d_out >= 0, d_in > 0");
+  if (!bits_ok(bits_a) || !bits_ok(bits_w)) return fail(OQ_EINVAL, "bits must be 2, 3, 4, 6 or 8");
+  if (!gemm_widths_ok(bits_a, bits_w)) return fail(OQ_EUNSUPPORTED, "no GEMM kernel for W%dA%d", bits_w, bits_a);
+  if (d_in % oq::ql_stage_k(bits_a) != 0)
+    return fail(OQ_EUNSUPPORTED, "d_in must be a multiple of %d for A%d", oq::ql_stage_k(bits_a), bits_a);
+  *bytes = 0;
+  if (T == 0 || d_out == 0) return ok();
+  int cus = 0;
+  oq_status st = device_cus(&cus);
+  if (st != OQ_OK) return st;
+  if (qlinear_plan(T, d_out, d_in, bits_a, cus, cus).sk_tiles > 0) *bytes = (size_t)oq::ql_ws_bytes(cus);
+  return ok();
+}
+
+oq_status oq_qlinear_splitk(const uint8_t* x_idx, const float* s, int64_t T, const uint8_t* w_idx,
+                            const float* w_norm, int32_t d_out, int32_t d_in, const double* centroids_a,
+                            int32_t bits_a, const double* centroids_w, int32_t bits_w, const float* bias,
+                            int32_t epilogue, void* y, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  oq::QlArgs a;
+  bool nothing = false;
+  oq_status st = qlinear_args(x_idx, s, T, w_idx, w_norm, d_out, d_in, centroids_a, bits_a, centroids_w, bits_w,
+                              bias, epilogue, y, &a, &nothing);
+  if (st != OQ_OK) return st;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return fail(OQ_EINVAL, "workspace must be 256-byte aligned");
+  if (nothing) return ok();
+  int cus = 0;
+  if ((st = device_cus(&cus)) != OQ_OK) return st;
+  const bool split = qlinear_plan(T, d_out, d_in, bits_a, cus, cus).sk_tiles > 0;
+  if (split) {
+    const size_t need = (size_t)oq::ql_ws_bytes(cus);
+    if (!workspace || workspace_bytes < need)
+      return fail(OQ_EINVAL, "workspace of %zu bytes needed (got %zu)", need, workspace ? workspace_bytes : (size_t)0);
+  }
+  return qlinear_launch(a, bits_a, bits_w, cus, static_cast<unsigned char*>(workspace), split ? cus : 0, stream);
 }
 
 oq_status oq_quantize_weights_int4(const void* W, oq_dtype w_dtype, int32_t d_out, int32_t d_in, int32_t group,

@@ -160,7 +160,8 @@ bool increasing(const std::vector<double>& c) {
 
 }  // namespace
 
-int lloyd_max_fd(int d, int bits, double* centroids, double* thresholds, double* mse_out, double* resid_out) {
+int lloyd_max_fd(int d, int bits, int max_newton, double* centroids, double* thresholds, double* mse_out,
+                 double* resid_out) {
   const Marginal f(d);
   const int L = 1 << bits;
   std::vector<double> c(L);
@@ -184,7 +185,7 @@ int lloyd_max_fd(int d, int bits, double* centroids, double* thresholds, double*
 
   std::vector<double> lo_d(L), di(L), up(L), rhs(L), step(L), cn(L);
   Eval en;
-  for (int it = 0; it < 300; ++it) {
+  for (int it = 0; it < max_newton; ++it) {
     double cmax = 0.0;
     for (double v : c) cmax = std::fmax(cmax, std::fabs(v));
     if (e.resid <= 1e-15 * cmax) break;

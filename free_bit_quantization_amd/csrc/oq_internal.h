@@ -6,14 +6,17 @@
 #include <cstdint>
 
 #include "oq.h"
+#include "ql_split.h"
 
 namespace oq {
 
 // ---- host math --------------------------------------------------------------
 void build_rpbh_tables(int32_t d, uint64_t seed, int32_t* perm, int8_t* sign);
 void build_block_rht_tables(int32_t d, uint64_t seed, int32_t* perm, int8_t* sign);
-// 0 on convergence (relative fixed-point residual <= 1e-10), -1 otherwise.
-int lloyd_max_fd(int d, int bits, double* centroids, double* thresholds, double* mse, double* resid);
+// 0 on convergence (relative fixed-point residual <= 1e-10), -1 otherwise;
+// at most max_newton Newton steps after the Lloyd steps.
+constexpr int kLloydMaxNewton = 300;
+int lloyd_max_fd(int d, int bits, int max_newton, double* centroids, double* thresholds, double* mse, double* resid);
 
 // ---- rotate-quantize (activations, fp32 fast path + fp64 recheck) ------------
 constexpr int kMaxThr = 255;     // 2^8 - 1 thresholds
@@ -85,17 +88,17 @@ struct QlArgs {
   int32_t epilogue;      // OQ_EPI_NONE / OQ_EPI_GELU_ERF, | OQ_EPI_OUT_BF16
   uint16_t tab_a[256];   // fp16 bits of sqrt(K) * c_a
   uint16_t tab_w[256];   // fp16 bits of sqrt(K) * c_w
-  // Work split (set by ql_launch): tiles [0, n_dp) are whole-tile work; the
-  // last sk_tiles tiles are split by K stages (stream-K, XCD by XCD, runs of
-  // at least sk_lmin stages); workgroups exchange fp32 partial tiles through ws
-  // (one 256 x 256 slot per workgroup) and flags (one word per workgroup, zero
-  // between launches).
-  int64_t n_dp;
-  int32_t sk_tiles;
-  int32_t sk_lmin;
-  float* ws;
+  // Work split over the persistent workgroups (ql_split.h).  With a split
+  // tail the workgroups exchange fp32 partial tiles through a workspace: hdr
+  // (launch generation, started-workgroup count), one flag per workgroup and
+  // one 256 x 256 slot per workgroup.
+  QlSplit sp;
+  uint32_t* hdr;
   uint32_t* flags;
+  float* slots;
 };
+// K indices per pipeline stage of the GEMM (a tile's K is cut into K / stage stages)
+inline int ql_stage_k(int bits_a) { return (bits_a == 8 || bits_a == 6) ? 64 : 128; }
 hipError_t ql_launch(const QlArgs& a, int bits_a, int bits_w, hipStream_t stream);
 
 // ---- INT4 round-to-nearest weight-only linear (AdaLN modulation) --------------

@@ -1,0 +1,181 @@
+// Work split of the codebook GEMM over its persistent workgroups.
+//
+// Shared by the host planner, the kernel and a CPU test of the arithmetic
+// (which compiles this header with a host compiler), so the split can be
+// checked exhaustively without a GPU: every (tile, K stage) of a launch is
+// computed exactly once, each tile of the split tail is finished by the one
+// workgroup that holds its last K stage, and that workgroup waits only on
+// workgroups with a lower index.
+//
+// A launch covers ntiles output tiles of 256 x 256, each nst K stages long.
+//  * Tiles [0, n_dp) are whole-tile work: a workgroup computes all nst stages
+//    of a tile and writes its outputs.
+//  * With a split, the last sk_tiles tiles (the tail: the last, partial round
+//    when there are more tiles than workgroups, else every tile) are cut along
+//    K.  Workgroup b belongs to class x = b % classes (classes = 8 when the
+//    grid is a multiple of 8: under the hardware's round-robin dealing of
+//    workgroups over the 8 XCDs a class then shares one XCD's L2; nothing
+//    depends on that for correctness).  Class x takes tiles [R x / C,
+//    R (x + 1) / C) of the R = sk_tiles tail tiles and cuts their S_x stages
+//    into rk runs of consecutive stages, run l = [S_x l / rk, S_x (l + 1) / rk)
+//    for the class's l-th workgroup.  Runs are at least lmin stages, so a tile
+//    has at most 4 pieces besides the one that finishes it, and never longer
+//    than a tile, so a run touches at most two tiles.
+//  * A piece that holds a tile's last stage finishes that tile: it adds the
+//    partial tiles the class's lower workgroups left for it, in a fixed order,
+//    and writes the outputs.  Any other piece leaves its partial tile in its
+//    workgroup's slot (one slot per workgroup: a run produces at most one
+//    partial) and raises its workgroup's flag.
+#ifndef OQ_QL_SPLIT_H_
+#define OQ_QL_SPLIT_H_
+
+#include <stdint.h>
+
+#if defined(__HIP__)
+#define OQ_HD __host__ __device__
+#else
+#define OQ_HD
+#endif
+
+namespace oq {
+
+struct QlSplit {
+  int64_t ntiles;    // output tiles of the launch
+  int64_t n_dp;      // whole tiles [0, n_dp)
+  int32_t sk_tiles;  // tail tiles split along K (0: no split)
+  int32_t nst;       // K stages per tile
+  int32_t lmin;      // shortest run (stages)
+  int32_t grid;      // workgroups
+  int32_t classes;   // workgroup classes (1 or 8)
+};
+
+// The plan: split the tail when a workspace with at least `slots` partial-tile
+// slots is available (slots >= the workgroup count), the tail holds at least 8
+// tiles, a tile has at least 4 stages and the tail would otherwise leave more
+// than a fifth of the `cus` workgroups idle.
+OQ_HD inline QlSplit ql_split_plan(int64_t ntiles, int32_t nst, int32_t cus, int64_t slots) {
+  QlSplit p;
+  p.ntiles = ntiles;
+  p.nst = nst;
+  p.n_dp = ntiles;
+  p.sk_tiles = 0;
+  p.lmin = 0;
+  p.classes = 1;
+  p.grid = (int32_t)(ntiles < cus ? ntiles : cus);
+  const int64_t full = ntiles / cus, rem = ntiles % cus;
+  if (slots >= cus && rem >= 8 && nst >= 4 && rem * 5 < (int64_t)cus * 4) {
+    p.grid = cus;
+    p.n_dp = full * cus;
+    p.sk_tiles = (int32_t)rem;
+    p.lmin = (nst + 3) / 4 > 2 ? (nst + 3) / 4 : 2;
+    p.classes = cus % 8 == 0 ? 8 : 1;
+  }
+  return p;
+}
+
+// ---- whole tiles -----------------------------------------------------------
+// Workgroup b takes tiles t0, t0 + tstep, ... below tend.  With a grid that is a
+// multiple of 8, class x owns a contiguous eighth of the whole tiles (so its
+// workgroups work on neighbouring tiles of the grouped raster order).
+OQ_HD inline void ql_dp_range(const QlSplit& p, int b, int64_t* t0, int64_t* tstep, int64_t* tend) {
+  if ((p.grid & 7) == 0) {
+    const int x = b & 7, loc = b >> 3, per = p.grid >> 3;
+    const int64_t q = p.n_dp / 8, rem = p.n_dp % 8;
+    const int64_t start = x * q + (x < rem ? x : rem);
+    *tend = start + q + (x < rem ? 1 : 0);
+    *t0 = start + loc;
+    *tstep = per;
+  } else {
+    *t0 = b;
+    *tstep = p.grid;
+    *tend = p.n_dp;
+  }
+}
+
+// ---- the split tail ----------------------------------------------------------
+struct QlClass {
+  int x, loc, nloc;   // class, index in the class, workgroups in the class
+  int64_t tx0, tx1;   // the class's tail tiles (indices among the tail tiles)
+  int64_t S;          // its K stages
+  int rk;             // its runs
+};
+
+OQ_HD inline QlClass ql_class(const QlSplit& p, int b) {
+  QlClass c;
+  const int C = p.classes;
+  c.x = b % C;
+  c.loc = b / C;
+  c.nloc = p.grid / C;
+  c.tx0 = (int64_t)p.sk_tiles * c.x / C;
+  c.tx1 = (int64_t)p.sk_tiles * (c.x + 1) / C;
+  c.S = (c.tx1 - c.tx0) * p.nst;
+  const int64_t rkx = p.lmin > 0 ? c.S / p.lmin : 0;
+  c.rk = (int)(rkx < c.nloc ? rkx : c.nloc);
+  return c;
+}
+
+// first stage of run l (class-local stage index)
+OQ_HD inline int64_t ql_bnd(const QlClass& c, int l) { return c.rk > 0 ? c.S * l / c.rk : 0; }
+
+// Number of pieces of the class's run of workgroup c.loc (0, 1 or 2).
+OQ_HD inline int ql_npieces(const QlSplit& p, const QlClass& c) {
+  if (p.sk_tiles == 0 || c.loc >= c.rk) return 0;
+  const int64_t u0 = ql_bnd(c, c.loc), u1 = ql_bnd(c, c.loc + 1);
+  if (u0 >= u1) return 0;
+  return u0 / p.nst == (u1 - 1) / p.nst ? 1 : 2;
+}
+
+// Piece k of the run, in execution order: with two pieces the producing one
+// (the head of the second tile) comes first, then the one that finishes the
+// first tile.  tile = class-local tail tile index; stages [s0, s1);
+// role 1 = leaves a partial, 2 = finishes the tile.
+OQ_HD inline void ql_piece(const QlSplit& p, const QlClass& c, int k, int64_t* tile, int* s0, int* s1, int* role) {
+  const int nst = p.nst;
+  const int64_t u0 = ql_bnd(c, c.loc), u1 = ql_bnd(c, c.loc + 1);
+  const int64_t tA = u0 / nst, tB = (u1 - 1) / nst;
+  if (tA == tB) {
+    *tile = tA;
+    *s0 = (int)(u0 - tA * nst);
+    *s1 = (int)(u1 - tA * nst);
+    *role = u1 == (tA + 1) * nst ? 2 : 1;
+  } else if (k == 0) {
+    *tile = tB;
+    *s0 = 0;
+    *s1 = (int)(u1 - tB * nst);
+    *role = 1;
+  } else {
+    *tile = tA;
+    *s0 = (int)(u0 - tA * nst);
+    *s1 = nst;
+    *role = 2;
+  }
+}
+
+// Contributors of the finishing piece of class-local tile `tile` held by
+// workgroup c.loc: the workgroups (grid indices, descending class index) whose
+// runs reach into the tile before it.  Returns their number, or -1 if there
+// are more than 4 (which the run lengths rule out).
+OQ_HD inline int ql_contributors(const QlSplit& p, const QlClass& c, int64_t tile, int out[4]) {
+  const int64_t U = tile * p.nst;   // the tile's first stage
+  int n = 0;
+  for (int l = c.loc - 1; l >= 0 && ql_bnd(c, l + 1) > U; --l) {
+    if (ql_bnd(c, l) == ql_bnd(c, l + 1)) continue;   // empty run
+    if (n == 4) return -1;
+    out[n++] = c.x + p.classes * l;
+  }
+  return n;
+}
+
+// ---- workspace layout ----------------------------------------------------------
+// [0, 256)            header: launch generation, finished-workgroup count
+// [256, 256 + F)      one 32-bit flag per workgroup slot (F = slots * 4, rounded up to 256)
+// [256 + F, ...)      slots of 256 x 256 fp32 partial tiles (256 KB each)
+constexpr int64_t kQlSlotBytes = 256 * 256 * 4;
+
+OQ_HD inline int64_t ql_ws_flags_offset() { return 256; }
+OQ_HD inline int64_t ql_ws_slots_offset(int64_t slots) { return 256 + ((slots * 4 + 255) / 256) * 256; }
+OQ_HD inline int64_t ql_ws_bytes(int64_t slots) { return ql_ws_slots_offset(slots) + slots * kQlSlotBytes; }
+
+}  // namespace oq
+
+#endif  // OQ_QL_SPLIT_H_

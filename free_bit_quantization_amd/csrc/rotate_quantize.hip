@@ -937,38 +937,43 @@ __global__ void __launch_bounds__(256) wq_kernel(const WqArgs a) {
   if (tid == 0) a.w_norm[o] = (float)n;
 }
 
-// Allow up to the 160 KB of LDS of a gfx950 CU (once per kernel instantiation).
+// Allow up to the 160 KB of LDS of a gfx950 CU (set on every launch: the
+// attribute belongs to the kernel and device, and the call is cheap, so no
+// host-side memo is kept).
 template <typename K>
-hipError_t allow_lds(K kernel, bool& done) {
-  if (done) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-  if (e == hipSuccess) done = true;
-  return e;
+hipError_t allow_lds(K kernel) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             160 * 1024);
 }
 
-int device_cus() {
-  static thread_local int cus = 0;
-  if (cus == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-      cus = 256;
-  }
-  return cus;
+hipError_t device_cus(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  return hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+}
+
+// Persistent grid: as many workgroups as are resident at once (capped by the
+// plan's own count), each looping over tokens.
+template <typename K>
+hipError_t resident_grid(K kernel, const RqPlan& p, int* grid) {
+  int per_cu = 0, cus = 0;
+  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, p.threads, p.lds);
+  if (e != hipSuccess) return e;
+  if ((e = device_cus(&cus)) != hipSuccess) return e;
+  const int64_t resident = (int64_t)(per_cu > 0 ? per_cu : 1) * cus;
+  *grid = (int)(p.grid < resident ? p.grid : resident);
+  return hipSuccess;
 }
 
 template <int LOG2H, bool BF16, int BITS>
 hipError_t rq_go(const RqArgs& a, const RqPlan& p, hipStream_t st) {
-  static thread_local bool attr = false;
-  hipError_t e = allow_lds(&rq_act_kernel<LOG2H, BF16, BITS>, attr);
+  auto kern = rq_act_kernel<LOG2H, BF16, BITS>;
+  hipError_t e = allow_lds(kern);
+  int grid = 0;
+  if (e == hipSuccess) e = resident_grid(kern, p, &grid);
   if (e != hipSuccess) return e;
-  // persistent grid: as many workgroups as are resident at once, each looping over tokens
-  int per_cu = 0;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, rq_act_kernel<LOG2H, BF16, BITS>, p.threads, p.lds);
-  if (e != hipSuccess) return e;
-  const int64_t resident = (int64_t)(per_cu > 0 ? per_cu : 1) * device_cus();
-  const int grid = (int)(p.grid < resident ? p.grid : resident);
-  hipLaunchKernelGGL((rq_act_kernel<LOG2H, BF16, BITS>), dim3(grid), dim3(p.threads), p.lds, st, a, p.ns, p.tpw);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(p.threads), p.lds, st, a, p.ns, p.tpw);
   return hipGetLastError();
 }
 
@@ -986,8 +991,7 @@ hipError_t rq_dispatch_bits(const RqArgs& a, int bits, const RqPlan& p, hipStrea
 
 template <bool BF16, int BITS>
 hipError_t wq_go(const WqArgs& a, size_t lds, hipStream_t st) {
-  static thread_local bool attr = false;
-  hipError_t e = allow_lds(&wq_kernel<BF16, BITS>, attr);
+  hipError_t e = allow_lds(&wq_kernel<BF16, BITS>);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((wq_kernel<BF16, BITS>), dim3(a.d_out), dim3(256), lds, st, a);
   return hipGetLastError();
@@ -1010,21 +1014,12 @@ hipError_t rq_dispatch(const RqArgs& a, int bits, const RqPlan& p, hipStream_t s
 
 template <int LOG2H, bool BF16, int BITS, int J>
 hipError_t rqw_go(const RqArgs& a, const RqPlan& p, hipStream_t st) {
-  static thread_local bool attr = false;
-  hipError_t e = allow_lds(&rq_wave_kernel<LOG2H, BF16, BITS, J>, attr);
+  auto kern = rq_wave_kernel<LOG2H, BF16, BITS, J>;
+  hipError_t e = allow_lds(kern);
+  int grid = 0;
+  if (e == hipSuccess) e = resident_grid(kern, p, &grid);
   if (e != hipSuccess) return e;
-  // resident workgroups per CU, cached per (threads, LDS bytes) of this instantiation
-  static thread_local int per_cu = 0, c_threads = 0;
-  static thread_local size_t c_lds = 0;
-  if (per_cu == 0 || c_threads != p.threads || c_lds != p.lds) {
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, rq_wave_kernel<LOG2H, BF16, BITS, J>, p.threads, p.lds);
-    if (e != hipSuccess) return e;
-    c_threads = p.threads;
-    c_lds = p.lds;
-  }
-  const int64_t resident = (int64_t)(per_cu > 0 ? per_cu : 1) * device_cus();
-  const int grid = (int)(p.grid < resident ? p.grid : resident);
-  hipLaunchKernelGGL((rq_wave_kernel<LOG2H, BF16, BITS, J>), dim3(grid), dim3(p.threads), p.lds, st, a, p.wpb);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(p.threads), p.lds, st, a, p.wpb);
   return hipGetLastError();
 }
 

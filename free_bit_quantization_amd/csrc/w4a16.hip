@@ -3,7 +3,7 @@
 // timestep-dependent scale and shift cannot absorb the rotation, and the
 // method keeps them at INT4 weight round-to-nearest ("OrbitQuant:
 // data-agnostic quantization for image and video", rcap.io summary:
-// deployment paragraph and AdaLN caveat; FLUX.2 Klein OrbitQuant W4A8 model
+// deployment paragraph and AdaLN caveat; "FLUX.3 Image Klein OrbitQuant W4A8" model
 // card, Components table).
 //
 // Scheme: symmetric signed codes q in [-8, 7]; one fp32 scale
@@ -260,13 +260,12 @@ hipError_t w4a_launch(const W4Args& a_in, bool bf16, hipStream_t st) {
   const int64_t gy = (a.T + a.tt - 1) / a.tt;   // token tiles
   if (gy > 65535) return hipErrorInvalidValue;
   const size_t lds = kTabBytes + kRedBytes + (size_t)tt * xstride;
-  static thread_local bool raised[2] = {false, false};
-  if (!raised[bf16]) {
+  {
+    // set on every launch (cheap; no host-side memo is kept)
     const void* fn = bf16 ? (const void*)w4a_kernel<true> : (const void*)w4a_kernel<false>;
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        kTabBytes + kRedBytes + kXLdsMax);
     if (e != hipSuccess) return e;
-    raised[bf16] = true;
   }
   const dim3 grid((unsigned)((a.N + kFeat - 1) / kFeat), (unsigned)gy);
   if (bf16) hipLaunchKernelGGL(w4a_kernel<true>, grid, dim3(kThreads), lds, st, a);

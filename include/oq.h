@@ -2,33 +2,38 @@
  * oq.h -- C ABI of liboq, the OrbitQuant quantized linear layer on AMD
  * Instinct MI355X (gfx950).
  *
- * The method (pages: "OrbitQuant: data-agnostic quantization for image and
- * video", rcap.io summary of the paper -- mechanism paragraphs and the
- * offline / online pseudo-code; "OrbitQuant quantizes FLUX.1 and Wan 2.1
- * with no calibration data", aiweekly.co):
+ * What the layer computes (method: "OrbitQuant: data-agnostic quantization
+ * for image and video", rcap.io summary of the paper -- the mechanism
+ * paragraphs and the offline / online pseudo-code; "OrbitQuant quantizes
+ * FLUX.1 and Wan 2.1 with no calibration data", aiweekly.co -- one codebook
+ * per input dimension).  For input dimension d let R = B D P be an orthogonal
+ * d x d matrix (P a seeded uniform permutation, D a seeded diagonal of +-1,
+ * B block-diagonal with h x h Walsh-Hadamard blocks scaled by 1/sqrt(h)), and
+ * let c_0 < ... < c_{L-1} be the L = 2^b levels of the Lloyd-Max quantizer of
+ * one coordinate of a uniformly random unit vector in R^d, with midpoints
+ * theta_j = (c_j + c_{j+1}) / 2.  Writing q(v)_k = #{j : theta_j < v_k} for
+ * the index vector of v:
  *
- *   offline, once per input dimension d:
- *     rotation[d]    = RPBH(d): random permutation, random sign flips,
- *                      block-diagonal Walsh-Hadamard blocks of size h
- *     codebook[d, b] = Lloyd-Max quantizer with 2^b centroids for the fixed
- *                      marginal f_d of one coordinate of a rotated unit vector
- *   offline, per weight matrix W (d_out x d_in):
- *     W_rot = W R^T; n = row norms; w_idx = nearest centroid of W_rot / n
- *   online, per token x:
- *     x_rot = R x; s = ||x_rot||; x_idx = nearest centroid of x_rot / (s + eps)
- *   layer output (the rotation cancels: W R^T R x = W x):
- *     y[t][o] = s_t n_o sum_k c_a[x_idx[t][k]] c_w[w_idx[o][k]]
+ *   weights, once:   n_o = |R w_o|,   iw_o = q(R w_o / (n_o + eps))
+ *   each token x_t:  s_t = |R x_t|,   ia_t = q(R x_t / (s_t + eps))
+ *   output:          y[t][o] = s_t n_o sum_k c^a_{ia_t,k} c^w_{iw_o,k}
+ *
+ * Since R is orthogonal (R^T R = I), y approximates W x: the product runs in
+ * the rotated basis and the rotation is never undone.
  *
  * Conventions for every call:
- *   - The caller owns every buffer; the library never allocates or frees.
- *     "dev" pointers are device memory on the current HIP device; "host"
- *     pointers are ordinary host memory read before the call returns.
+ *   - The caller owns every buffer, workspaces included; the library never
+ *     allocates or frees.  "dev" pointers are device memory on the current
+ *     HIP device; "host" pointers are ordinary host memory read before the
+ *     call returns.
  *   - Arguments are validated before anything is launched.  Invalid
  *     arguments return OQ_EINVAL and touch nothing; a shape or bit width with
  *     no kernel returns OQ_EUNSUPPORTED; a HIP launch / device error returns
  *     OQ_EDEVICE.  oq_last_error() gives a message for the calling thread.
  *   - Device calls are asynchronous and stream-ordered: OQ_OK means enqueued
- *     on `stream` (0 = the null stream).  T = 0 is a valid no-op.
+ *     on `stream` (0 = the null stream).  T = 0 is a valid no-op.  No call
+ *     synchronises, allocates or issues a memset, so device calls can be
+ *     captured into HIP graphs.
  *   - Index order: index 0 is the most negative centroid.  Packed indices are
  *     row-major, contiguous along d_in; index k of a row occupies bits
  *     [k b, (k+1) b) of the row read as a little-endian bit stream.  For
@@ -115,14 +120,18 @@ oq_status oq_build_block_rht(int32_t d, int32_t h, uint64_t seed, int32_t* perm,
  * mse        : host double or NULL: E[(t - Q(t))^2] under f_d.
  * Errors     : OQ_EINVAL (bad d / bits / NULL); OQ_ENOCONV if the relative
  *              fixed-point residual stays above 1e-10 (outputs still written).
+ * The solve takes at most 300 Newton steps; the environment variable
+ * OQ_LLOYD_MAX_NEWTON_STEPS = n (0 <= n < 300) lowers that cap, which lets
+ * the OQ_ENOCONV path be exercised.
  */
 oq_status oq_lloyd_max(int32_t d, int32_t bits, double* centroids, double* thresholds, double* mse);
 
 /*
- * oq_quantize_weights -- the offline weight step of the pseudo-code:
- * W_rot = W R^T, n_o = ||W_rot[o]||, w_idx[o] = nearest centroid of
- * W_rot[o] / (n_o + OQ_EPS), i.e. #{j : thresholds[j] < u}.  Computed in fp64
- * on the device (offline, not on the hot path).
+ * oq_quantize_weights -- the offline weight step (rcap.io summary, offline
+ * part of the pseudo-code): for each weight row w_o, n_o = |R w_o| and
+ * w_idx[o] = q(R w_o / (n_o + OQ_EPS)), q(v)_k = #{j : thresholds[j] < v_k}
+ * (the index of the nearest centroid).  Computed in fp64 on the device
+ * (offline, not on the hot path).
  *
  * W          : dev [d_out][d_in], fp32 or bf16 (w_dtype), row-major.
  * d_out      : >= 0 rows.   d_in: dimension, h | d_in, d_in * bits_w % 8 == 0.
@@ -140,9 +149,9 @@ oq_status oq_quantize_weights(const void* W, oq_dtype w_dtype, int32_t d_out, in
                               uint8_t* w_idx, float* w_norm, hipStream_t stream);
 
 /*
- * oq_rotate_quantize_act -- the online activation step of the pseudo-code,
- * per token: x_rot = R x (fast block Hadamard, O(d log h)), s = ||x_rot||,
- * x_idx = #{j : thresholds[j] < x_rot / (s + OQ_EPS)}.  Hot path.
+ * oq_rotate_quantize_act -- the online activation step (rcap.io summary,
+ * online part of the pseudo-code), per token x: v = R x (fast block Hadamard,
+ * O(d log h)), s = |v|, x_idx = q(v / (s + OQ_EPS)).  Hot path.
  *
  * The rotation runs in fp32.  A coordinate whose fp32 value lies within a
  * certified rounding bound of a decision threshold is recomputed in fp64 and
@@ -178,25 +187,8 @@ oq_status oq_rotate_quantize_act(const void* x, oq_dtype x_dtype, int64_t T, int
  *
  * Indices are decoded through LDS tables of fp16(sqrt(d_in) * c) into fp16
  * MFMA operands with fp32 accumulation; the epilogue scales by
- * s * w_norm / d_in.  Hot path.
- *
- * The last, partial round of 256 x 256 output tiles (all tiles, when there
- * are fewer than the device's CUs) is split by K (stream-K) when it holds at
- * least 8 tiles and would leave more than a fifth of the CUs idle: the
- * workgroups of each XCD exchange fp32 partial tiles through a workspace that
- * the library owns, one per (device, stream): cus * 256 KB plus cus flags,
- * allocated on the first such launch on that stream and kept until the
- * process ends (at most 16 streams per device; past that, while the stream is
- * being captured into a graph and has no workspace yet, or on a device whose
- * workgroups are not dealt round-robin over 8 XCDs, the launch runs whole
- * tiles).  The first such launch on a device also runs a small probe kernel
- * of the XCD dispatch and synchronises its stream once.  The partial tiles
- * are added in a fixed order, so results are deterministic; launches that
- * share a stream are ordered by it.  A graph captured on a stream that
- * already has a workspace records that workspace: replay it only ordered
- * with the other launches that use it (on the capture stream, or after them);
- * two split launches that overlap on one workspace race, and the tiles whose
- * exchange fails come out as NaN.
+ * s * w_norm / d_in.  Hot path.  Persistent workgroups (one per compute unit)
+ * compute whole 256 x 256 output tiles; no workspace.
  *
  * x_idx       : dev [T][d_in * bits_a / 8], from oq_rotate_quantize_act.
  * s           : dev [T] float.
@@ -223,11 +215,63 @@ oq_status oq_qlinear(const uint8_t* x_idx, const float* s, int64_t T,
                      const float* bias, int32_t epilogue, void* y, hipStream_t stream);
 
 /*
+ * oq_qlinear_workspace_size -- bytes of workspace oq_qlinear_splitk needs for
+ * this shape on the current device: 0 if the shape takes no split, else
+ * 256 + 4 cus (rounded up to 256) + cus * 256 KB for a device with cus
+ * compute units (64 MB + 1280 bytes on a 256-CU MI355X).  The same passages
+ * as oq_qlinear.
+ *
+ * T, d_out, d_in, bits_a, bits_w : as for oq_qlinear.
+ * bytes   : host size_t, written.
+ * Errors  : OQ_EINVAL, OQ_EUNSUPPORTED, OQ_EDEVICE (no device to query).
+ */
+oq_status oq_qlinear_workspace_size(int64_t T, int32_t d_out, int32_t d_in, int32_t bits_a, int32_t bits_w,
+                                    size_t* bytes);
+
+/*
+ * oq_qlinear_splitk -- oq_qlinear (same passages, same result up to fp32
+ * summation order, deterministic) with the last, partial round of output
+ * tiles split along K: when a launch has a partial last round (or fewer
+ * tiles than compute units) that holds at least 8 tiles and would leave
+ * more than a fifth of the compute units idle, the workgroups cut that
+ * round's K stages into equal runs, and the workgroup that holds a tile's
+ * last stage adds the fp32 partial tiles the others left in the workspace,
+ * in a fixed order, before the epilogue (stream-K).  Other shapes run as
+ * oq_qlinear and ignore the workspace.
+ *
+ * workspace       : dev, 256-byte aligned, at least the bytes that
+ *                   oq_qlinear_workspace_size gives for this shape (NULL / 0
+ *                   is fine when it gives 0).  Caller-owned.  It must be
+ *                   zero-filled once before its first use; every launch
+ *                   leaves its control words ready for the next one (a launch
+ *                   generation that each launch advances, and per-workgroup
+ *                   flags tagged with it), so later launches need no clearing.
+ *                   Launches that share a workspace must be ordered (one
+ *                   stream, or events): two launches running at once on one
+ *                   workspace race, and their tiles can come out wrong.  A
+ *                   graph that captures a launch records the workspace.
+ * workspace_bytes : its size.
+ * Other arguments : as oq_qlinear.
+ * A finishing workgroup waits for its contributors with a bounded spin;
+ * contributors never wait and are dispatched before it, so the bound is
+ * reached only if the device stops dispatching them (then that tile is
+ * written as NaN; the status, returned at enqueue time, cannot show it).
+ * Errors          : OQ_EINVAL (also: workspace missing, too small or
+ *                   misaligned), OQ_EUNSUPPORTED, OQ_EDEVICE.
+ */
+oq_status oq_qlinear_splitk(const uint8_t* x_idx, const float* s, int64_t T,
+                            const uint8_t* w_idx, const float* w_norm, int32_t d_out, int32_t d_in,
+                            const double* centroids_a, int32_t bits_a,
+                            const double* centroids_w, int32_t bits_w,
+                            const float* bias, int32_t epilogue, void* y,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * oq_quantize_weights_int4 -- INT4 round-to-nearest, weight only, for the
  * AdaLN modulation projections, which the method keeps out of the codebooks:
  * their timestep-dependent scale and shift cannot absorb the rotation
- * (rcap.io summary: deployment paragraph and AdaLN caveat; FLUX.2 Klein
- * OrbitQuant W4A8 model card, Components table).  The pages name only "INT4
+ * (rcap.io summary: deployment paragraph and AdaLN caveat; "FLUX.3 Image
+ * Klein OrbitQuant W4A8" model card, Components table).  The pages name only "INT4
  * weight round-to-nearest"; the scheme here is symmetric:
  *
  *   s[o][g] = fp32(max_{k in g} |W[o][k]| / 7)      (fp64 division)

@@ -8,8 +8,8 @@ timestep-dependent scale and shift, so the rotation trick does not apply to
 them and they are kept at INT4 weight round-to-nearest while every other
 projection of the block is OrbitQuant-quantized ("OrbitQuant: data-agnostic
 quantization for image and video", rcap.io summary: the deployment paragraph
-and the AdaLN caveat; the FLUX.2 Klein OrbitQuant W4A8 model card, Components
-table: INT4 for the modulation projections).
+and the AdaLN caveat; the "FLUX.3 Image Klein OrbitQuant W4A8" model card,
+Components table: INT4 for the modulation projections).
 
 The pages say no more than "INT4 weight round-to-nearest". Readings (the
 plainest scheme that name covers):

@@ -162,10 +162,24 @@ def check_weights(W: np.ndarray, h: int, bits: int, seed: int = 0, name: str = "
     return w_idx, w_norm, rep
 
 
+def run_gemm(x_idx, s, w_idx, w_norm, d, bits_a, bits_w, ca, cw, bias=None, epilogue=0, split=False, out_dtype=None,
+             workspace=None):
+    """One GEMM launch: oq_qlinear (whole tiles), or oq_qlinear_splitk with a
+    zero-filled workspace of the size the library asks for (or the one given)."""
+    if not split:
+        return oq.oq_qlinear(x_idx, s, w_idx, w_norm, d, ca, bits_a, cw, bits_w, bias=bias, epilogue=epilogue,
+                             out_dtype=out_dtype)
+    if workspace is None:
+        workspace = oq.qlinear_workspace(s.shape[0], w_norm.shape[0], d, bits_a, bits_w)
+    return oq.oq_qlinear_splitk(x_idx, s, w_idx, w_norm, d, ca, bits_a, cw, bits_w, workspace, bias=bias,
+                                epilogue=epilogue, out_dtype=out_dtype)
+
+
 def check_gemm(x_idx, s, w_idx, w_norm, d: int, bits_a: int, bits_w: int, bias=None, gelu=False,
-               rows: Optional[np.ndarray] = None, name: str = "", out_dtype=None):
+               rows: Optional[np.ndarray] = None, name: str = "", out_dtype=None, split=False, workspace=None):
     """GEMM on the GPU vs the oracle's dequantized product of the GPU's own indices.
 
+    split=True runs oq_qlinear_splitk (stream-K tail through a workspace).
     With out_dtype=torch.bfloat16 the GEMM also runs with bf16 output; that
     tensor must hold the fp32 output rounded to nearest even, bit for bit
     (report key "bf16_equal"), and it is the one returned."""
@@ -173,8 +187,9 @@ def check_gemm(x_idx, s, w_idx, w_norm, d: int, bits_a: int, bits_w: int, bias=N
     ca = library_codebook(d, bits_a)
     cw = library_codebook(d, bits_w)
     bd = None if bias is None else torch.from_numpy(bias).cuda()
-    y = oq.oq_qlinear(x_idx, s, w_idx, w_norm, d, ca.c, bits_a, cw.c, bits_w, bias=bd,
-                      epilogue=oq.OQ_EPI_GELU_ERF if gelu else oq.OQ_EPI_NONE)
+    epi = oq.OQ_EPI_GELU_ERF if gelu else oq.OQ_EPI_NONE
+    y = run_gemm(x_idx, s, w_idx, w_norm, d, bits_a, bits_w, ca.c, cw.c, bias=bd, epilogue=epi, split=split,
+                 workspace=workspace)
     torch.cuda.synchronize()
     T = s.shape[0]
     rows = np.arange(T) if rows is None else rows
@@ -184,11 +199,11 @@ def check_gemm(x_idx, s, w_idx, w_norm, d: int, bits_a: int, bits_w: int, bias=N
                                     bias=bias, gelu=gelu)
     yg = y.cpu().numpy()[rows]
     err = rel_frob(yg, ref)
-    rep = {"name": name, "T": T, "N": w_norm.shape[0], "K": d, "checked_rows": len(rows), "rel_frob": err,
+    rep = {"name": name, "split": split, "T": T, "N": w_norm.shape[0], "K": d, "checked_rows": len(rows), "rel_frob": err,
            "tile_rel_max": tile_rel_max(yg, ref, rows), "finite": bool(np.all(np.isfinite(yg)))}
     if out_dtype is not None:
-        y16 = oq.oq_qlinear(x_idx, s, w_idx, w_norm, d, ca.c, bits_a, cw.c, bits_w, bias=bd,
-                            epilogue=oq.OQ_EPI_GELU_ERF if gelu else oq.OQ_EPI_NONE, out_dtype=out_dtype)
+        y16 = run_gemm(x_idx, s, w_idx, w_norm, d, bits_a, bits_w, ca.c, cw.c, bias=bd, epilogue=epi, split=split,
+                       out_dtype=out_dtype, workspace=workspace)
         torch.cuda.synchronize()
         rep["bf16_equal"] = bool(torch.equal(y16.view(torch.int16), y.to(out_dtype).view(torch.int16)))
         y = y16

@@ -211,8 +211,11 @@ def test_gemm_repeatable():
 
 
 def _gemm_twice(lin, rows, seed, bias=False, gelu=False):
-    """The GEMM on two scale vectors in a row, every tile of both checked: the
-    second launch must not consume the first one's partial tiles."""
+    """oq_qlinear_splitk on two scale vectors in a row through one workspace,
+    every tile of both checked: the second launch must not consume the first
+    one's partial tiles.  Then oq_qlinear (whole tiles) on the same inputs:
+    the tiles that neither launch splits are bit-identical."""
+    from free_bit_quantization_amd import oq
     x, Wm = synth.gen_linear(lin, seed, 0)
     x_idx, s, ra = P.check_activations(x, lin.act_dtype, lin.h, lin.bits_a, rows=np.arange(min(8, lin.T)),
                                        want_x_rot=False, name=lin.name)
@@ -220,22 +223,41 @@ def _gemm_twice(lin, rows, seed, bias=False, gelu=False):
     w_idx, w_norm, rw = P.check_weights(Wm, lin.h, lin.bits_w, name=lin.name)
     _assert_w(rw)
     b = synth.gen_bias(lin.d_out, seed) if bias else None
+    ws = oq.qlinear_workspace(lin.T, lin.d_out, lin.d_in, lin.bits_a, lin.bits_w)
+    assert ws is not None, "the shape is expected to take the split"
+    ys = []
     for k, scale in enumerate((1.0, 1.75)):
         sk = s * scale
-        _, rg = P.check_gemm(x_idx, sk, w_idx, w_norm, lin.d_in, lin.bits_a, lin.bits_w, bias=b, gelu=gelu,
-                             rows=rows, name=f"{lin.name}-launch{k}")
+        y, rg = P.check_gemm(x_idx, sk, w_idx, w_norm, lin.d_in, lin.bits_a, lin.bits_w, bias=b, gelu=gelu,
+                             rows=rows, name=f"{lin.name}-launch{k}", split=True, workspace=ws)
         _assert_gemm(rg)
+        ys.append(y)
+    y_whole, rg = P.check_gemm(x_idx, s * 1.75, w_idx, w_norm, lin.d_in, lin.bits_a, lin.bits_w, bias=b, gelu=gelu,
+                               rows=rows, name=f"{lin.name}-whole")
+    _assert_gemm(rg)
+    return ys[1], y_whole
+
+
+def _untouched_tiles_equal(y_split, y_whole, T, N, n_dp):
+    # tiles [0, n_dp) of the grouped raster order are computed the same way by
+    # both entry points; compare the rows of every 256-row block whose tiles
+    # all come before the split (the raster walks 4 block rows at a time)
+    ntn = (N + 255) // 256
+    full_groups = n_dp // (4 * ntn)
+    r = min(T, full_groups * 4 * 256)
+    assert torch.equal(y_split[:r], y_whole[:r])
+    return r
 
 
 @pytest.mark.parametrize("T,d,d_out,bits_w,bits_a", [(1024, 3072, 3072, 4, 8), (1024, 12288, 3072, 4, 8),
                                                      (2100, 1024, 300, 4, 4), (1000, 1024, 2000, 2, 4),
-                                                     (512, 1024, 1024, 4, 4),    # 8 tiles: one per XCD, 4 pieces
+                                                     (512, 1024, 1024, 4, 4),    # 8 tiles: one per class, 4 pieces
                                                      (2048, 512, 1024, 4, 4),    # 4 K stages per tile
                                                      (1024, 1024, 1024, 6, 6)])  # 6-bit widths (128 x 64 blocks)
 def test_stream_k_split_tiles(T, d, d_out, bits_w, bits_a):
-    # fewer tiles than CUs (18 to 48, some ragged): every tile is split by K
-    # stages over 2-5 workgroups of one XCD (stream-K); bias and GELU on the
-    # ragged shape (the finisher applies them after summing the partials)
+    # fewer tiles than CUs (8 to 48, some ragged): every tile is split by K
+    # stages over 2-5 workgroups (stream-K); bias and GELU on the ragged shape
+    # (the finisher applies them after summing the partials)
     lin = synth.Linear(f"sk-{T}x{d}x{d_out}", T, d, d_out, 256, bits_w, bits_a, "student_t", "bf16", 10, 30.0,
                        0.5, 5, 10.0)
     ragged = d_out % 256 != 0
@@ -244,10 +266,40 @@ def test_stream_k_split_tiles(T, d, d_out, bits_w, bits_a):
 
 def test_flux_qkv_last_round_tiles_twice():
     # 648 tiles on 256 CUs: two whole rounds, then the last 136 tiles (M rows
-    # 3072 .. 4607 in the grouped raster order) split by K stages, 17 per XCD;
-    # checked tile by tile, on two launches in a row
+    # 3072 .. 4607 in the grouped raster order) split by K stages, 17 per
+    # class; checked tile by tile on two launches in a row; the first two
+    # rounds bit-identical to the whole-tile entry point
     lin = W["flux_qkv_w4a4"].linears[0]
-    _gemm_twice(lin, np.arange(3072, lin.T), seed=5)
+    y_split, y_whole = _gemm_twice(lin, np.arange(3072, lin.T), seed=5)
+    assert _untouched_tiles_equal(y_split, y_whole, lin.T, lin.d_out, 512) == 3072
+
+
+def test_split_workspace_size_and_rejection():
+    from free_bit_quantization_amd import oq
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n = oq.oq_qlinear_workspace_size(4608, 9216, 3072, 4, 4)
+    slots_off = 256 + ((4 * cus + 255) // 256) * 256
+    assert n == slots_off + cus * 256 * 256 * 4, (n, cus)
+    assert oq.oq_qlinear_workspace_size(256, 256, 3072, 4, 4) == 0       # one tile: no split
+    assert oq.oq_qlinear_workspace_size(4608, 1024, 3072, 4, 4) == n     # 72 tiles: split
+    lin = synth.Linear("ws", 512, 1024, 1024, 256, 4, 4, "student_t", "bf16", 10, 30.0, 0.5, 5, 10.0)
+    x, Wm = synth.gen_linear(lin, 1, 0)
+    x_idx, s, _ = P.check_activations(x, "bf16", 256, 4, rows=np.arange(4), want_x_rot=False)
+    w_idx, w_norm, _ = P.check_weights(Wm, 256, 4)
+    cb = P.library_codebook(1024, 4)
+    need = oq.oq_qlinear_workspace_size(512, 1024, 1024, 4, 4)
+    assert need > 0
+    small = torch.zeros(need - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(oq.OQError) as e:
+        oq.oq_qlinear_splitk(x_idx, s, w_idx, w_norm, 1024, cb.c, 4, cb.c, 4, small)
+    assert e.value.status == oq.OQ_EINVAL and "workspace" in str(e.value)
+    with pytest.raises(oq.OQError):
+        oq.oq_qlinear_splitk(x_idx, s, w_idx, w_norm, 1024, cb.c, 4, cb.c, 4, None)
+    # a shape without a split ignores the workspace
+    y = oq.oq_qlinear_splitk(x_idx[:1], s[:1], w_idx[:256], w_norm[:256], 1024, cb.c, 4, cb.c, 4, None)
+    y0 = oq.oq_qlinear(x_idx[:1], s[:1], w_idx[:256], w_norm[:256], 1024, cb.c, 4, cb.c, 4)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y0)
 
 
 # ---- bf16 output: the fp32 result rounded to nearest even, bit for bit -----------
@@ -267,9 +319,10 @@ def test_gemm_bf16_output_is_rounded_fp32(T, d, d_out, bits_w, bits_a, gelu):
     cw = P.library_codebook(d, bits_w)
     bias = torch.from_numpy(synth.gen_bias(d_out, 2)).cuda()
     epi = oq.OQ_EPI_GELU_ERF if gelu else oq.OQ_EPI_NONE
-    y32 = oq.oq_qlinear(x_idx, s, w_idx, w_norm, d, ca.c, bits_a, cw.c, bits_w, bias=bias, epilogue=epi)
-    y16 = oq.oq_qlinear(x_idx, s, w_idx, w_norm, d, ca.c, bits_a, cw.c, bits_w, bias=bias, epilogue=epi,
-                        out_dtype=torch.bfloat16)
+    split = T * d_out >= 1024 * 3072     # the third case takes the stream-K split
+    y32 = P.run_gemm(x_idx, s, w_idx, w_norm, d, bits_a, bits_w, ca.c, cw.c, bias=bias, epilogue=epi, split=split)
+    y16 = P.run_gemm(x_idx, s, w_idx, w_norm, d, bits_a, bits_w, ca.c, cw.c, bias=bias, epilogue=epi, split=split,
+                     out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert y16.dtype == torch.bfloat16
     assert torch.equal(y16.view(torch.int16), y32.to(torch.bfloat16).view(torch.int16))

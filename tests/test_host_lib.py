@@ -157,3 +157,113 @@ def test_int4_rtn_entry_points_reject_invalid_arguments():
     assert lw(f, oq.OQ_F16, 0, f, f, 64, 256, 256, None, f, None) == oq.OQ_OK       # T = 0: no-op
     assert lw(f, oq.OQ_BF16, 4, f, f, 0, 256, 128, None, f, None) == oq.OQ_OK       # d_out = 0: no-op
     assert oq.lib().oq_last_error() is not None
+
+
+def test_split_gemm_entry_points_reject_invalid_arguments():
+    # only rejected calls, queries that need no device and no-ops
+    L = oq.lib()
+    f = _fake()
+    g = _fake((1 << 20) + 4)
+    c, _, _ = oq.oq_lloyd_max(256, 4)
+    cp = c.ctypes.data
+    sk = L.oq_qlinear_splitk
+    assert sk(f, f, 4, f, f, 8, 256, cp, 4, cp, 5, None, 0, f, f, 1 << 30, None) == oq.OQ_EINVAL   # bits_w
+    assert sk(None, f, 4, f, f, 8, 256, cp, 4, cp, 4, None, 0, f, f, 1 << 30, None) == oq.OQ_EINVAL
+    assert sk(f, f, 4, f, f, 8, 256, cp, 4, cp, 4, None, 0, g, f, 1 << 30, None) == oq.OQ_EINVAL    # y alignment
+    assert sk(f, f, 4, f, f, 8, 256, cp, 4, cp, 4, None, 0, f, _fake((1 << 20) + 16), 1 << 30,
+              None) == oq.OQ_EINVAL                                                                  # workspace alignment
+    assert b"256-byte" in L.oq_last_error()
+    assert sk(f, f, 4, f, f, 8, 96, cp, 4, cp, 4, None, 0, f, f, 1 << 30, None) == oq.OQ_EUNSUPPORTED
+    assert sk(f, f, 0, f, f, 8, 256, cp, 4, cp, 4, None, 0, f, None, 0, None) == oq.OQ_OK            # T = 0
+    ws = L.oq_qlinear_workspace_size
+    n = ctypes.c_size_t(123)
+    assert ws(4, 8, 256, 4, 4, None) == oq.OQ_EINVAL
+    assert ws(-1, 8, 256, 4, 4, ctypes.addressof(n)) == oq.OQ_EINVAL
+    assert ws(4, 8, 256, 5, 4, ctypes.addressof(n)) == oq.OQ_EINVAL
+    assert ws(4, 8, 256, 2, 4, ctypes.addressof(n)) == oq.OQ_EUNSUPPORTED     # A2: no kernel
+    assert ws(4, 8, 96, 4, 4, ctypes.addressof(n)) == oq.OQ_EUNSUPPORTED      # d_in not a multiple of 128
+    assert ws(0, 8, 256, 4, 4, ctypes.addressof(n)) == oq.OQ_OK and n.value == 0
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:  # pragma: no cover
+        return False
+
+
+@pytest.mark.skipif(_gpu_visible(), reason="needs a host without a visible GPU (the calls would launch)")
+def test_device_calls_without_a_device_return_edevice():
+    # valid arguments on a host with no HIP device: the call reaches the
+    # runtime, which reports no device; nothing can launch
+    L = oq.lib()
+    f = _fake()
+    c, th, _ = oq.oq_lloyd_max(256, 4)
+    cp, thp = c.ctypes.data, th.ctypes.data
+    assert L.oq_qlinear(f, f, 4, f, f, 8, 256, cp, 4, cp, 4, None, 0, f, None) == oq.OQ_EDEVICE
+    assert L.oq_last_error()
+    assert L.oq_qlinear_splitk(f, f, 4, f, f, 8, 256, cp, 4, cp, 4, None, 0, f, None, 0, None) == oq.OQ_EDEVICE
+    n = ctypes.c_size_t(0)
+    assert L.oq_qlinear_workspace_size(4608, 9216, 3072, 4, 4, ctypes.addressof(n)) == oq.OQ_EDEVICE
+    assert L.oq_rotate_quantize_act(f, oq.OQ_BF16, 4, 256, 64, f, f, thp, 4, f, f, None, None) == oq.OQ_EDEVICE
+    assert L.oq_quantize_weights(f, oq.OQ_F32, 4, 256, 64, f, f, thp, 4, f, f, None) == oq.OQ_EDEVICE
+
+
+@pytest.mark.parametrize("d,bits,steps", [(3072, 8, 0), (3072, 8, 2), (256, 4, 0), (12288, 4, 0)])
+def test_lloyd_max_reports_non_convergence(monkeypatch, d, bits, steps):
+    # with the Newton steps capped, the Lloyd steps alone leave the fixed-point
+    # residual above 1e-10: OQ_ENOCONV, outputs still written (and ordered)
+    L = oq.lib()
+    n = 1 << bits
+    c = np.full(n, np.nan)
+    t = np.full(n - 1, np.nan)
+    monkeypatch.setenv("OQ_LLOYD_MAX_NEWTON_STEPS", str(steps))
+    assert L.oq_lloyd_max(d, bits, c.ctypes.data, t.ctypes.data, None) == oq.OQ_ENOCONV
+    assert b"residual" in L.oq_last_error()
+    assert np.all(np.isfinite(c)) and np.all(np.diff(c) > 0)
+    np.testing.assert_array_equal(t, 0.5 * (c[:-1] + c[1:]))
+    monkeypatch.delenv("OQ_LLOYD_MAX_NEWTON_STEPS")
+    assert L.oq_lloyd_max(d, bits, c.ctypes.data, t.ctypes.data, None) == oq.OQ_OK
+    monkeypatch.setenv("OQ_LLOYD_MAX_NEWTON_STEPS", "garbage")   # not a count: the default cap
+    assert L.oq_lloyd_max(d, bits, c.ctypes.data, t.ctypes.data, None) == oq.OQ_OK
+
+
+def test_binding_checks_shapes_tables_and_devices_before_calling():
+    # host tensors: every check that precedes the device check fires here,
+    # and a well-shaped host tensor is refused as not being on the device
+    torch = pytest.importorskip("torch")
+    c, th, _ = oq.oq_lloyd_max(256, 4)
+    T, d, n = 8, 256, 16
+    x_idx = torch.zeros((T, d // 2), dtype=torch.uint8)
+    s = torch.zeros(T)
+    w_idx = torch.zeros((n, d // 2), dtype=torch.uint8)
+    w_norm = torch.zeros(n)
+    with pytest.raises(ValueError, match="centroids_a"):
+        oq.oq_qlinear(x_idx, s, w_idx, w_norm, d, c[:8], 4, c, 4)
+    with pytest.raises(ValueError, match="centroids_w"):
+        oq.oq_qlinear(x_idx, s, w_idx, w_norm, d, c, 4, np.append(c, 0.0), 4)
+    with pytest.raises(ValueError, match="x_idx"):
+        oq.oq_qlinear(x_idx[:, :64], s, w_idx, w_norm, d, c, 4, c, 4)
+    with pytest.raises(ValueError, match="w_idx"):
+        oq.oq_qlinear(x_idx, s, w_idx[:-1], w_norm, d, c, 4, c, 4)
+    with pytest.raises(ValueError, match="x_idx"):
+        oq.oq_qlinear(x_idx, s, w_idx, w_norm, 128, c, 4, c, 4)             # d_in disagrees with the indices
+    with pytest.raises(ValueError, match="bias"):
+        oq.oq_qlinear(x_idx, s, w_idx, w_norm, d, c, 4, c, 4, bias=torch.zeros(n + 1))
+    with pytest.raises(TypeError, match="s: expected torch.float32"):
+        oq.oq_qlinear(x_idx, s.double(), w_idx, w_norm, d, c, 4, c, 4)
+    with pytest.raises(TypeError, match="device"):
+        oq.oq_qlinear(x_idx, s, w_idx, w_norm, d, c, 4, c, 4)
+    with pytest.raises(ValueError, match="thresholds"):
+        oq.oq_rotate_quantize_act(torch.zeros((T, d)), 64, torch.zeros(d, dtype=torch.int32),
+                                  torch.zeros(d, dtype=torch.int8), th[:-1], 4)
+    with pytest.raises(ValueError, match="perm"):
+        oq.oq_rotate_quantize_act(torch.zeros((T, d)), 64, torch.zeros(d - 1, dtype=torch.int32),
+                                  torch.zeros(d, dtype=torch.int8), th, 4)
+    with pytest.raises(ValueError, match="thresholds"):
+        oq.oq_quantize_weights(torch.zeros((n, d)), 64, torch.zeros(d, dtype=torch.int32),
+                               torch.zeros(d, dtype=torch.int8), np.append(th, 1.0), 4)
+    with pytest.raises(ValueError, match="whole bytes"):
+        oq.oq_rotate_quantize_act(torch.zeros((T, 250)), 2, torch.zeros(250, dtype=torch.int32),
+                                  torch.zeros(250, dtype=torch.int8), oq.oq_lloyd_max(250, 3)[1], 3)

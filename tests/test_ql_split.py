@@ -1,0 +1,80 @@
+"""The codebook GEMM's work split, checked on the CPU.
+
+ql_split.h holds the arithmetic the kernel uses to divide a launch among its
+persistent workgroups: whole tiles first, then the last partial round of tiles
+cut along K (stream-K) when the caller gives a workspace.  tests/ql_split_check.cpp
+compiles that header with the host compiler and enumerates what every
+workgroup computes, checking that each (tile, K stage) is computed once, that
+each split tile has one finisher whose contributor list is exactly the
+workgroups that left it a partial (at most 4, all with lower indices, so no
+wait can be on a workgroup dispatched after the waiter), and that a workgroup
+leaves at most one partial (one workspace slot each)."""
+
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "free_bit_quantization_amd", "csrc")
+SRC = os.path.join(ROOT, "tests", "ql_split_check.cpp")
+
+
+@pytest.fixture(scope="module")
+def checker(tmp_path_factory):
+    cxx = shutil.which("g++") or shutil.which("c++")
+    if cxx is None:
+        pytest.skip("no host C++ compiler")
+    exe = str(tmp_path_factory.mktemp("qlsplit") / "ql_split_check")
+    subprocess.run([cxx, "-std=c++17", "-O2", "-Wall", "-Werror", f"-I{CSRC}", SRC, "-o", exe], check=True)
+    return exe
+
+
+def _run(exe, *args):
+    r = subprocess.run([exe] + [str(a) for a in args], stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    assert r.returncode == 0 and r.stdout.startswith("ok"), r.stdout
+    return r.stdout
+
+
+def _tiles(T, N):
+    return ((T + 255) // 256) * ((N + 255) // 256)
+
+
+def _stages(K, bits_a):
+    return K // (64 if bits_a in (6, 8) else 128)
+
+
+# every linear of the five workloads, and the shapes of the GPU stream-K tests
+SHAPES = [
+    (64, 256, 256, 4),                                            # single linear
+    (4608, 3072, 9216, 4),                                        # FLUX QKV
+    (4608, 3072, 12288, 4), (4608, 12288, 3072, 4),               # FLUX MLP pair
+    (32760, 5120, 13824, 4),                                      # Wan FFN
+    (8192, 3072, 9216, 8), (8192, 3072, 3072, 8), (8192, 3072, 12288, 8), (8192, 12288, 3072, 8),
+    (1024, 3072, 9216, 8), (1024, 3072, 3072, 8), (1024, 3072, 12288, 8), (1024, 12288, 3072, 8),
+    (1024, 3072, 3072, 8), (1024, 12288, 3072, 8), (2100, 1024, 300, 4), (1000, 1024, 2000, 4),
+    (512, 1024, 1024, 4), (2048, 512, 1024, 4), (1024, 1024, 1024, 6), (520, 1024, 777, 4),
+    (700, 3072, 1030, 4),
+]
+
+
+@pytest.mark.parametrize("T,K,N,bits_a", SHAPES)
+@pytest.mark.parametrize("cus", [256, 304, 80])
+def test_split_of_workload_shapes(checker, T, K, N, bits_a, cus):
+    _run(checker, _tiles(T, N), _stages(K, bits_a), cus)
+
+
+def test_flux_qkv_takes_the_split_on_256_cus(checker):
+    out = _run(checker, _tiles(4608, 9216), _stages(3072, 4), 256)
+    # 648 tiles: two whole rounds, the last 136 tiles split along K, 8 classes
+    assert "n_dp=512 sk_tiles=136 grid=256 classes=8" in out, out
+
+
+def test_no_split_without_slots(checker):
+    out = _run(checker, _tiles(4608, 9216), _stages(3072, 4), 256, 0)
+    assert "n_dp=648 sk_tiles=0 grid=256" in out, out
+
+
+def test_sweep_of_tile_counts_stages_and_cu_counts(checker):
+    _run(checker, "sweep")
