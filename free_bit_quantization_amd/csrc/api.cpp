@@ -342,6 +342,30 @@ oq_status oq_qlinear_splitk(const uint8_t* x_idx, const float* s, int64_t T, con
   return qlinear_launch(a, bits_a, bits_w, cus, static_cast<unsigned char*>(workspace), split ? cus : 0, stream);
 }
 
+oq_status oq_qlinear_splitk_noalloc(const uint8_t* x_idx, const float* s, int64_t T, const uint8_t* w_idx,
+                                    const float* w_norm, int32_t d_out, int32_t d_in, const double* centroids_a,
+                                    int32_t bits_a, const double* centroids_w, int32_t bits_w, const float* bias,
+                                    int32_t epilogue, void* y, hipStream_t stream) {
+  static_assert(oq::kScratchBytes == oq::ql_ws_bytes(oq::kScratchSlots), "scratch layout");
+  oq::QlArgs a;
+  bool nothing = false;
+  oq_status st = qlinear_args(x_idx, s, T, w_idx, w_norm, d_out, d_in, centroids_a, bits_a, centroids_w, bits_w,
+                              bias, epilogue, y, &a, &nothing);
+  if (st != OQ_OK) return st;
+  if (nothing) return ok();
+  int cus = 0;
+  if ((st = device_cus(&cus)) != OQ_OK) return st;
+  const bool split = qlinear_plan(T, d_out, d_in, bits_a, cus, cus).sk_tiles > 0;
+  if (!split) return qlinear_launch(a, bits_a, bits_w, cus, nullptr, 0, stream);
+  if (cus > oq::kScratchSlots)
+    return fail(OQ_EUNSUPPORTED, "the split needs %d partial-tile slots; the library scratch holds %d", cus,
+                oq::kScratchSlots);
+  void* ws = nullptr;
+  hipError_t e = oq::ql_scratch(&ws);
+  if (e != hipSuccess) return device_error(e, "library scratch address");
+  return qlinear_launch(a, bits_a, bits_w, cus, static_cast<unsigned char*>(ws), oq::kScratchSlots, stream);
+}
+
 oq_status oq_quantize_weights_int4(const void* W, oq_dtype w_dtype, int32_t d_out, int32_t d_in, int32_t group,
                                    uint8_t* q, float* scale, hipStream_t stream) {
   if (w_dtype != OQ_F32 && w_dtype != OQ_BF16) return fail(OQ_EINVAL, "w_dtype must be OQ_F32 or OQ_BF16");

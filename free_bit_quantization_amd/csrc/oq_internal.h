@@ -100,6 +100,11 @@ struct QlArgs {
 // K indices per pipeline stage of the GEMM (a tile's K is cut into K / stage stages)
 inline int ql_stage_k(int bits_a) { return (bits_a == 8 || bits_a == 6) ? 64 : 128; }
 hipError_t ql_launch(const QlArgs& a, int bits_a, int bits_w, hipStream_t stream);
+// The library's fixed device scratch for the split GEMM (oq_qlinear_splitk_noalloc):
+// a workspace laid out for kScratchSlots slots; *ptr = its address on the current device.
+constexpr int kScratchSlots = 256;
+constexpr int64_t kScratchBytes = 256 + ((kScratchSlots * 4 + 255) / 256) * 256 + (int64_t)kScratchSlots * 256 * 256 * 4;
+hipError_t ql_scratch(void** ptr);
 
 // ---- INT4 round-to-nearest weight-only linear (AdaLN modulation) --------------
 struct RtnArgs {

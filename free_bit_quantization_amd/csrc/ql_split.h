@@ -167,14 +167,14 @@ OQ_HD inline int ql_contributors(const QlSplit& p, const QlClass& c, int64_t til
 }
 
 // ---- workspace layout ----------------------------------------------------------
-// [0, 256)            header: launch generation, finished-workgroup count
+// [0, 256)            header: launch generation, workgroups started in this launch
 // [256, 256 + F)      one 32-bit flag per workgroup slot (F = slots * 4, rounded up to 256)
 // [256 + F, ...)      slots of 256 x 256 fp32 partial tiles (256 KB each)
 constexpr int64_t kQlSlotBytes = 256 * 256 * 4;
 
-OQ_HD inline int64_t ql_ws_flags_offset() { return 256; }
-OQ_HD inline int64_t ql_ws_slots_offset(int64_t slots) { return 256 + ((slots * 4 + 255) / 256) * 256; }
-OQ_HD inline int64_t ql_ws_bytes(int64_t slots) { return ql_ws_slots_offset(slots) + slots * kQlSlotBytes; }
+OQ_HD constexpr int64_t ql_ws_flags_offset() { return 256; }
+OQ_HD constexpr int64_t ql_ws_slots_offset(int64_t slots) { return 256 + ((slots * 4 + 255) / 256) * 256; }
+OQ_HD constexpr int64_t ql_ws_bytes(int64_t slots) { return ql_ws_slots_offset(slots) + slots * kQlSlotBytes; }
 
 }  // namespace oq
 

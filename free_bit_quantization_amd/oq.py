@@ -25,7 +25,7 @@ OQ_EPI_NONE, OQ_EPI_GELU_ERF, OQ_EPI_OUT_BF16 = 0, 1, 0x100
 # every symbol include/oq.h declares
 EXPORTS = ("oq_last_error", "oq_version", "oq_build_rpbh", "oq_build_block_rht", "oq_lloyd_max",
            "oq_quantize_weights", "oq_rotate_quantize_act", "oq_qlinear", "oq_qlinear_workspace_size",
-           "oq_qlinear_splitk", "oq_quantize_weights_int4", "oq_linear_w4a16")
+           "oq_qlinear_splitk", "oq_qlinear_splitk_noalloc", "oq_quantize_weights_int4", "oq_linear_w4a16")
 
 
 class OQError(RuntimeError):
@@ -70,6 +70,8 @@ def lib() -> ctypes.CDLL:
         L.oq_qlinear_splitk.restype = _I32
         L.oq_qlinear_splitk.argtypes = [_P, _P, _I64, _P, _P, _I32, _I32, _P, _I32, _P, _I32, _P, _I32, _P, _P,
                                         ctypes.c_size_t, _P]
+        L.oq_qlinear_splitk_noalloc.restype = _I32
+        L.oq_qlinear_splitk_noalloc.argtypes = [_P, _P, _I64, _P, _P, _I32, _I32, _P, _I32, _P, _I32, _P, _I32, _P, _P]
         L.oq_quantize_weights_int4.restype = _I32
         L.oq_quantize_weights_int4.argtypes = [_P, _I32, _I32, _I32, _I32, _P, _P, _P]
         L.oq_linear_w4a16.restype = _I32
@@ -300,6 +302,18 @@ def oq_qlinear_splitk(x_idx, s, w_idx, w_norm, d_in: int, centroids_a, bits_a: i
     else:
         wp, wn = _dev(workspace, torch.uint8, what="workspace"), workspace.numel()
     _check(lib().oq_qlinear_splitk(*args, wp, wn, _stream(stream)))
+    return y
+
+
+def oq_qlinear_splitk_noalloc(x_idx, s, w_idx, w_norm, d_in: int, centroids_a, bits_a: int, centroids_w,
+                              bits_w: int, bias=None, epilogue: int = OQ_EPI_NONE, y=None, stream=None,
+                              out_dtype=None):
+    """oq_qlinear_splitk through the library's own device scratch (no
+    workspace argument; calls on one device must not overlap).  Allocates
+    y only when it is not given."""
+    y, args, _keep = _qlinear_args(x_idx, s, w_idx, w_norm, d_in, centroids_a, bits_a, centroids_w, bits_w, bias,
+                                   epilogue, y, out_dtype)
+    _check(lib().oq_qlinear_splitk_noalloc(*args, _stream(stream)))
     return y
 
 

@@ -23,7 +23,8 @@
  *
  * Conventions for every call:
  *   - The caller owns every buffer, workspaces included; the library never
- *     allocates or frees.  "dev" pointers are device memory on the current
+ *     allocates or frees (oq_qlinear_splitk_noalloc uses a static device
+ *     array instead of a workspace).  "dev" pointers are device memory on the current
  *     HIP device; "host" pointers are ordinary host memory read before the
  *     call returns.
  *   - Arguments are validated before anything is launched.  Invalid
@@ -39,7 +40,8 @@
  *     [k b, (k+1) b) of the row read as a little-endian bit stream.  For
  *     b = 2, 4, 8 that is least-significant bits first within each byte (4, 2,
  *     1 per byte); 3- and 6-bit indices straddle byte boundaries.
- *   - The only global state is the thread-local error message.
+ *   - The only global state is the thread-local error message, and the
+ *     device scratch of oq_qlinear_splitk_noalloc with its address per device.
  */
 #ifndef OQ_H_
 #define OQ_H_
@@ -265,6 +267,31 @@ oq_status oq_qlinear_splitk(const uint8_t* x_idx, const float* s, int64_t T,
                             const double* centroids_w, int32_t bits_w,
                             const float* bias, int32_t epilogue, void* y,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * oq_qlinear_splitk_noalloc -- oq_qlinear_splitk without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * split's workspace is the library's own fixed device scratch: 64 MB + 1280
+ * bytes (256 partial-tile slots), a static device array that every device
+ * the library runs on holds from the moment the library's code is loaded
+ * until the process ends; this call allocates nothing and calls no
+ * allocating routine.  Results are bit-identical to oq_qlinear_splitk with a
+ * workspace of its own.
+ *
+ * Every call on one device shares that device's scratch, which keeps the
+ * last call's contents (its launch generation advances each call, so nothing
+ * needs clearing): calls that can run at the same time on one device (other
+ * streams, graphs) race, and their tiles can come out wrong; order them.
+ * Arguments and result as oq_qlinear.
+ * Errors : as oq_qlinear; OQ_EUNSUPPORTED if the split would need more than
+ *          the scratch's 256 slots (a device with more than 256 compute units).
+ */
+oq_status oq_qlinear_splitk_noalloc(const uint8_t* x_idx, const float* s, int64_t T,
+                                    const uint8_t* w_idx, const float* w_norm, int32_t d_out, int32_t d_in,
+                                    const double* centroids_a, int32_t bits_a,
+                                    const double* centroids_w, int32_t bits_w,
+                                    const float* bias, int32_t epilogue, void* y, hipStream_t stream);
 
 /*
  * oq_quantize_weights_int4 -- INT4 round-to-nearest, weight only, for the
