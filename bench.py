@@ -169,10 +169,13 @@ def measure_linear(lin, index, steps, warmup, ring_mb, dev, split=True):
     return r
 
 
-def measure_mlp(up, down, hidden, steps, warmup, ring_mb, dev):
+def measure_mlp(up, down, hidden, steps, warmup, ring_mb, dev, folded=False):
     """Time the chained MLP pair: rotate-quantize x, up GEMM with the GELU
     epilogue into the hidden state h, rotate-quantize h, down GEMM.  h is
-    fp32 or bf16 (the up GEMM rounds its output to nearest even)."""
+    fp32 or bf16 (the up GEMM rounds its output to nearest even).  folded:
+    the down rotation's permutation folded into the up projection's rows
+    (oq_fold_permutation, offline), so the down rotate-quantize gathers with
+    the identity permutation."""
     import torch
     from free_bit_quantization_amd import oq, synth
 
@@ -190,6 +193,12 @@ def measure_mlp(up, down, hidden, steps, warmup, ring_mb, dev):
         Wd = torch.from_numpy(Wm).to(dev)
         wq.append(oq.oq_quantize_weights(Wd, hb, *rot[lin.d_in], cb[(lin.d_in, lin.bits_w)][1], lin.bits_w))
         del Wd
+    bias_up = torch.from_numpy(synth.gen_bias(H, 3)).to(dev)
+    rq_down_tables = rot[H]
+    if folded:
+        wi, wn, bias_up = oq.oq_fold_permutation(wq[0][0], wq[0][1], rot[H][0], K, up.bits_w, bias=bias_up)
+        wq[0] = (wi, wn)
+        rq_down_tables = (torch.arange(H, dtype=torch.int32, device=dev), rot[H][1])
     xt = torch.from_numpy(x).to(dev).to(torch.bfloat16)
     nring = max(1, math.ceil(ring_mb * 1e6 / (xt.numel() * xt.element_size())))
     ring = [xt] + [torch.roll(xt, shifts=i * 7, dims=0).contiguous() for i in range(1, nring)]
@@ -206,9 +215,9 @@ def measure_mlp(up, down, hidden, steps, warmup, ring_mb, dev):
         yield lambda: oq.oq_rotate_quantize_act(ring[i % nring], hb, *rot[K], cb[(K, up.bits_a)][1], up.bits_a,
                                                 x_idx=xi_u, s=s_u, stream=stream)
         yield lambda: oq.oq_qlinear(xi_u, s_u, wq[0][0], wq[0][1], K, cb[(K, up.bits_a)][0], up.bits_a,
-                                    cb[(K, up.bits_w)][0], up.bits_w, epilogue=oq.OQ_EPI_GELU_ERF, y=hbuf,
-                                    stream=stream)
-        yield lambda: oq.oq_rotate_quantize_act(hbuf, hb, *rot[H], cb[(H, down.bits_a)][1], down.bits_a,
+                                    cb[(K, up.bits_w)][0], up.bits_w, bias=bias_up, epilogue=oq.OQ_EPI_GELU_ERF,
+                                    y=hbuf, stream=stream)
+        yield lambda: oq.oq_rotate_quantize_act(hbuf, hb, *rq_down_tables, cb[(H, down.bits_a)][1], down.bits_a,
                                                 x_idx=xi_d, s=s_d, stream=stream)
         yield lambda: oq.oq_qlinear(xi_d, s_d, wq[1][0], wq[1][1], H, cb[(H, down.bits_a)][0], down.bits_a,
                                     cb[(H, down.bits_w)][0], down.bits_w, y=y, stream=stream)
@@ -231,12 +240,16 @@ def measure_mlp(up, down, hidden, steps, warmup, ring_mb, dev):
     ms_step = start.elapsed_time(end) / steps
     per = [sum(e[j].elapsed_time(e[j + 1]) for e in ev) / steps for j in range(4)]
     flops = 2.0 * T * K * H + 2.0 * T * H * N
-    return {"workload": "flux_mlp_chain", "hidden": hidden, "tokens": T, "d_in": K, "d_hidden": H, "d_out": N,
+    rq_down_bytes = T * H * hbuf.element_size() + T * H * down.bits_a // 8 + 4 * T
+    return {"workload": "flux_mlp_chain", "hidden": hidden, "folded_permutation": folded,
+            "tokens": T, "d_in": K, "d_hidden": H, "d_out": N,
             "bits_w": up.bits_w, "bits_a": up.bits_a, "h": hb, "hidden_bytes": T * H * hbuf.element_size(),
             "ms_per_step": round(ms_step, 5), "tokens_per_s": round(T / (ms_step * 1e-3), 1),
             "TFLOPs": round(flops / (ms_step * 1e-3) / 1e12, 2),
             "rq_up_ms": round(per[0], 5), "gemm_up_ms": round(per[1], 5), "rq_down_ms": round(per[2], 5),
-            "gemm_down_ms": round(per[3], 5), "activation_ring_buffers": nring}
+            "gemm_down_ms": round(per[3], 5), "rq_down_GBps": round(rq_down_bytes / (per[2] * 1e-3) / 1e9, 1),
+            "rq_down_frac_hbm": round(rq_down_bytes / (per[2] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "activation_ring_buffers": nring}
 
 
 def measure_modulation(lin, steps, warmup, ring_mb, dev):
@@ -336,8 +349,10 @@ def main():
     if args.mlp:
         up, down = synth.workloads()["flux_mlp_w2a4"].linears
         for hidden in ("f32", "bf16"):
-            print(json.dumps(measure_mlp(up, down, hidden, args.steps, args.warmup, args.ring_mb, dev)), flush=True)
-            torch.cuda.empty_cache()
+            for folded in (False, True):
+                print(json.dumps(measure_mlp(up, down, hidden, args.steps, args.warmup, args.ring_mb, dev, folded)),
+                      flush=True)
+                torch.cuda.empty_cache()
         return
 
     if args.sweep:

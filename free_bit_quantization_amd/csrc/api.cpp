@@ -366,6 +366,31 @@ oq_status oq_qlinear_splitk_noalloc(const uint8_t* x_idx, const float* s, int64_
   return qlinear_launch(a, bits_a, bits_w, cus, static_cast<unsigned char*>(ws), oq::kScratchSlots, stream);
 }
 
+oq_status oq_fold_permutation(const uint8_t* w_idx, const float* w_norm, const float* bias, int32_t d_out,
+                              int32_t d_in, int32_t bits_w, const int32_t* perm_next, uint8_t* w_idx_out,
+                              float* w_norm_out, float* bias_out, hipStream_t stream) {
+  if (d_out < 0 || d_in <= 0) return fail(OQ_EINVAL, "need d_out >= 0 and d_in > 0");
+  if (!bits_ok(bits_w)) return fail(OQ_EINVAL, "bits_w must be 2, 3, 4, 6 or 8 (got %d)", bits_w);
+  const int64_t row_bytes = (int64_t)d_in * bits_w / 8;
+  if (((int64_t)d_in * bits_w) % 128 != 0) return fail(OQ_EINVAL, "d_in * bits_w / 8 must be a multiple of 16");
+  if (d_out == 0) return ok();
+  if (!w_idx || !w_norm || !perm_next || !w_idx_out || !w_norm_out || (bias && !bias_out))
+    return fail(OQ_EINVAL, "NULL device pointer");
+  auto misaligned = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) != 0; };
+  if (misaligned(w_idx) || misaligned(w_idx_out)) return fail(OQ_EINVAL, "w_idx and w_idx_out must be 16-byte aligned");
+  auto overlap = [](const void* a, const void* b, int64_t n) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + (uintptr_t)n && y < x + (uintptr_t)n;
+  };
+  if (overlap(w_idx, w_idx_out, (int64_t)d_out * row_bytes) || overlap(w_norm, w_norm_out, 4 * (int64_t)d_out) ||
+      (bias && overlap(bias, bias_out, 4 * (int64_t)d_out)))
+    return fail(OQ_EINVAL, "outputs must not overlap the inputs");
+  oq::FoldArgs a{w_idx, w_norm, bias, perm_next, d_out, row_bytes, w_idx_out, w_norm_out, bias_out};
+  hipError_t e = oq::fold_launch(a, stream);
+  if (e != hipSuccess) return device_error(e, "oq_fold_permutation launch");
+  return ok();
+}
+
 oq_status oq_quantize_weights_int4(const void* W, oq_dtype w_dtype, int32_t d_out, int32_t d_in, int32_t group,
                                    uint8_t* q, float* scale, hipStream_t stream) {
   if (w_dtype != OQ_F32 && w_dtype != OQ_BF16) return fail(OQ_EINVAL, "w_dtype must be OQ_F32 or OQ_BF16");

@@ -52,6 +52,7 @@ struct RqPlan {
   size_t lds;    // dynamic LDS bytes
   int wave_j;    // > 0: one wavefront per token, wave_j slots of 16 coordinates per lane
   int wpb;       // wavefronts per workgroup of that kernel
+  int pad;       // workgroup kernel: staged rows padded (16 coordinates per 256)
 };
 
 // Returns false if (d, h) has no kernel.
@@ -105,6 +106,20 @@ hipError_t ql_launch(const QlArgs& a, int bits_a, int bits_w, hipStream_t stream
 constexpr int kScratchSlots = 256;
 constexpr int64_t kScratchBytes = 256 + ((kScratchSlots * 4 + 255) / 256) * 256 + (int64_t)kScratchSlots * 256 * 256 * 4;
 hipError_t ql_scratch(void** ptr);
+
+// ---- folding the next layer's permutation into the output channels -----------
+struct FoldArgs {
+  const uint8_t* w_idx;   // [rows][row_bytes]
+  const float* w_norm;    // [rows]
+  const float* bias;      // [rows] or null
+  const int32_t* perm;    // [rows]
+  int64_t rows;
+  int64_t row_bytes;      // multiple of 16
+  uint8_t* w_idx_out;
+  float* w_norm_out;
+  float* bias_out;
+};
+hipError_t fold_launch(const FoldArgs& a, hipStream_t stream);
 
 // ---- INT4 round-to-nearest weight-only linear (AdaLN modulation) --------------
 struct RtnArgs {

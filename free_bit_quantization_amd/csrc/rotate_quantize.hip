@@ -104,6 +104,18 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 
 __host__ __device__ inline size_t align16(size_t v) { return (v + 15) & ~size_t(15); }
 
+// Staged rows are padded by 16 coordinates after every 256: coordinate i of a
+// row sits at lds_pos(i).  The gathers read, for a fixed element index, one
+// run of 16 coordinates per 256-block; without the padding every block's run
+// falls on the same LDS banks (a 256-coordinate block spans a whole number of
+// bank rows), which is what an identity or block-diagonal permutation (a folded
+// permutation, Block-RHT) would read.  With it the blocks of a wavefront use
+// different banks.  Random permutations are unaffected.
+// (The workgroup kernel pads only when its layout still fits the LDS: pad = 0
+// or 1 below.)
+__host__ __device__ constexpr int lds_pos(int i, int pad = 1) { return i + pad * 16 * (i >> 8); }
+__host__ __device__ constexpr int lds_row(int d, int pad = 1) { return d + pad * 16 * ((d + 255) >> 8); }
+
 // Packed indices of one 16-coordinate slot: index r occupies bits
 // [r BITS, (r+1) BITS) of a little-endian stream held in 32-bit words (the
 // row layout of the index arrays); 2 BITS bytes are stored.
@@ -184,13 +196,13 @@ struct RqLayout {
   size_t lut, thr, row, trans, red, total, row_stride;  // row_stride: bytes of one parity buffer
 };
 
-__host__ __device__ inline RqLayout rq_layout(int d, int log2h, int es, int tpw, int G) {
+__host__ __device__ inline RqLayout rq_layout(int d, int log2h, int es, int tpw, int G, int pad) {
   RqLayout L;
   const int h = 1 << log2h;
   L.lut = 0;
   L.thr = align16(8 * (size_t)(G > 0 ? G : 1));
   L.row = L.thr + 2 * 256 * 4;   // thr, then thr_lo
-  L.row_stride = align16((size_t)tpw * d * es);
+  L.row_stride = align16((size_t)tpw * lds_row(d, pad) * es);
   L.trans = L.row + 2 * L.row_stride;
   const size_t trans_bytes = log2h > 4 ? (size_t)tpw * (d / h) * (h + kPad) * 4 : 0;
   L.red = L.trans + align16(trans_bytes);
@@ -220,7 +232,7 @@ __device__ __forceinline__ int count_below_exact_from(const float* thr, const fl
 }
 
 template <int LOG2H, bool BF16, int BITS>
-__global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int NS, const int TPW) {
+__global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int NS, const int TPW, const int PAD) {
   constexpr int H = 1 << LOG2H;
   constexpr int ES = BF16 ? 2 : 4;
   constexpr bool TWO_PASS = LOG2H > 4;
@@ -239,7 +251,7 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
   const int nthr = a.nthr;
 
   extern __shared__ __align__(16) unsigned char smem[];
-  const RqLayout Ly = rq_layout(d, LOG2H, ES, TPW, G);
+  const RqLayout Ly = rq_layout(d, LOG2H, ES, TPW, G, PAD);
   int2* lut = reinterpret_cast<int2*>(smem + Ly.lut);
   float* thr = reinterpret_cast<float*>(smem + Ly.thr);
   double* red = reinterpret_cast<double*>(smem + Ly.red);
@@ -275,7 +287,7 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
   for (int r = 0; r < 16; ++r) {
     const int gi = gin(r);
     const int src = min((unsigned)a.perm[gi], (unsigned)(d - 1));  // perm is a permutation of 0..d-1
-    addr[r] = (uint32_t)(Ly.row + ((size_t)tl * d + src) * ES);
+    addr[r] = (uint32_t)(Ly.row + ((size_t)tl * lds_row(d, PAD) + lds_pos(src, PAD)) * ES);
     sgn[r] = a.sign[gi] < 0 ? 0x80000000u : 0u;
   }
   __syncthreads();
@@ -306,7 +318,8 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
     // ---- 1. stage the prefetched coordinates [16 sl, 16 sl + 16), sum of squares
     double q0 = 0.0, q1 = 0.0, q2 = 0.0, q3 = 0.0;   // exact squares, fp64 sums
     {
-      u32x4* rowdst = reinterpret_cast<u32x4*>(smem + Ly.row + paroff + ((size_t)tl * d + 16 * sl) * ES);
+      u32x4* rowdst = reinterpret_cast<u32x4*>(smem + Ly.row + paroff +
+                                               ((size_t)tl * lds_row(d, PAD) + lds_pos(16 * sl, PAD)) * ES);
 #pragma unroll
       for (int k = 0; k < NV; ++k) rowdst[k] = raw[k];
       if (BF16) {
@@ -546,7 +559,7 @@ __host__ __device__ inline RqwLayout rqw_layout(int d, int log2h, int es, int G,
   const size_t mwords = es == 2 ? (size_t)d / 2 : (size_t)d;   // sign masks of the source words
   L.atab = L.mtab + align16(4 * mwords);                          // gather offsets, 4 d bytes
   L.wave0 = L.atab + align16(4 * (size_t)d);
-  L.row_bytes = align16((size_t)d * es);
+  L.row_bytes = align16((size_t)lds_row(d) * es);
   L.wave_bytes = L.row_bytes + align16((size_t)(1024 / h) * (h + kPad) * 4);
   L.total = L.wave0 + (size_t)wpb * L.wave_bytes;
   const size_t setup = L.wave0 + align16((size_t)d);   // sign' bytes over the wave buffers
@@ -633,7 +646,7 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
     const int i = tid + k * (int)blockDim.x;
     if (i < d) {
       sp[pj[k]] = sj[k];
-      atab[i] = (uint32_t)pa[k] * ES;
+      atab[i] = (uint32_t)lds_pos(pa[k]) * ES;
     }
   }
   __syncthreads();
@@ -669,7 +682,7 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
     for (int i = 0; i < J; ++i) {
       const int k = lane + 64 * i;   // chunk: coordinates [16 k, 16 k + 16)
       const u32x4* mk = reinterpret_cast<const u32x4*>(mtab + k * MW);
-      u32x4* dst = reinterpret_cast<u32x4*>(wrow + (size_t)16 * k * ES);
+      u32x4* dst = reinterpret_cast<u32x4*>(wrow + (size_t)lds_pos(16 * k) * ES);
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
         const u32x4 m = mk[v];
@@ -794,7 +807,7 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
           double sx = 0.0;
 #pragma unroll
           for (int i = 0; i < J; ++i) {
-            const u32x4* src = reinterpret_cast<const u32x4*>(wrow + (size_t)16 * (lane + 64 * i) * ES);
+            const u32x4* src = reinterpret_cast<const u32x4*>(wrow + (size_t)lds_pos(16 * (lane + 64 * i)) * ES);
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
               const u32x4 w = src[v];
@@ -973,7 +986,7 @@ hipError_t rq_go(const RqArgs& a, const RqPlan& p, hipStream_t st) {
   int grid = 0;
   if (e == hipSuccess) e = resident_grid(kern, p, &grid);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(p.threads), p.lds, st, a, p.ns, p.tpw);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(p.threads), p.lds, st, a, p.ns, p.tpw, p.pad);
   return hipGetLastError();
 }
 
@@ -1068,6 +1081,7 @@ bool rq_plan(int32_t d, int32_t log2h, bool bf16, int64_t T, int G, RqPlan* p) {
   const int ns = d / 16;
   p->wave_j = 0;
   p->wpb = 0;
+  p->pad = 1;
   // one wavefront per token: d = 1024 J with J <= 5 (bf16) or J <= 2 (fp32: the
   // prefetched row takes twice the registers), h in {64, 256}, grid search
   if (ns % 64 == 0 && ns / 64 <= (bf16 ? 5 : 2) && (log2h == 6 || log2h == 8) && G > 0) {
@@ -1100,7 +1114,9 @@ bool rq_plan(int32_t d, int32_t log2h, bool bf16, int64_t T, int G, RqPlan* p) {
   p->ns = ns;
   p->tpw = tpw;
   p->threads = ns * tpw;
-  const RqLayout L = rq_layout(d, log2h, bf16 ? 2 : 4, tpw, G);
+  p->pad = 1;
+  if (rq_layout(d, log2h, bf16 ? 2 : 4, tpw, G, 1).total > 160 * 1024) p->pad = 0;   // pad only if it fits
+  const RqLayout L = rq_layout(d, log2h, bf16 ? 2 : 4, tpw, G, p->pad);
   p->lds = L.total;
   if (p->lds > 160 * 1024) return false;
   const int64_t groups = (T + tpw - 1) / tpw;

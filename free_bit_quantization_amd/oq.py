@@ -25,7 +25,8 @@ OQ_EPI_NONE, OQ_EPI_GELU_ERF, OQ_EPI_OUT_BF16 = 0, 1, 0x100
 # every symbol include/oq.h declares
 EXPORTS = ("oq_last_error", "oq_version", "oq_build_rpbh", "oq_build_block_rht", "oq_lloyd_max",
            "oq_quantize_weights", "oq_rotate_quantize_act", "oq_qlinear", "oq_qlinear_workspace_size",
-           "oq_qlinear_splitk", "oq_qlinear_splitk_noalloc", "oq_quantize_weights_int4", "oq_linear_w4a16")
+           "oq_qlinear_splitk", "oq_qlinear_splitk_noalloc", "oq_fold_permutation", "oq_quantize_weights_int4",
+           "oq_linear_w4a16")
 
 
 class OQError(RuntimeError):
@@ -72,6 +73,8 @@ def lib() -> ctypes.CDLL:
                                         ctypes.c_size_t, _P]
         L.oq_qlinear_splitk_noalloc.restype = _I32
         L.oq_qlinear_splitk_noalloc.argtypes = [_P, _P, _I64, _P, _P, _I32, _I32, _P, _I32, _P, _I32, _P, _I32, _P, _P]
+        L.oq_fold_permutation.restype = _I32
+        L.oq_fold_permutation.argtypes = [_P, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P]
         L.oq_quantize_weights_int4.restype = _I32
         L.oq_quantize_weights_int4.argtypes = [_P, _I32, _I32, _I32, _I32, _P, _P, _P]
         L.oq_linear_w4a16.restype = _I32
@@ -202,6 +205,30 @@ def oq_quantize_weights(W, h: int, perm, sign, thresholds, bits_w: int, w_idx=No
                                      _dev(w_idx, torch.uint8, (d_out, cols), "w_idx"),
                                      _dev(w_norm, torch.float32, (d_out,), "w_norm"), _stream(stream)))
     return w_idx, w_norm
+
+
+def oq_fold_permutation(w_idx, w_norm, perm_next, d_in: int, bits_w: int, bias=None, stream=None):
+    """Offline: this layer's quantized rows reordered by the next layer's RPBH
+    permutation (out[i] = in[perm_next[i]]): returns (w_idx, w_norm, bias or
+    None), new tensors.  The next rotate-quantize of GELU(y) then takes the
+    identity permutation with its own signs."""
+    import torch
+    d_out = w_norm.shape[0]
+    cols = _packed_cols(d_in, bits_w, "w_idx")
+    _meta(w_idx, torch.uint8, (d_out, cols), "w_idx")
+    _meta(w_norm, torch.float32, (d_out,), "w_norm")
+    _meta(perm_next, torch.int32, (d_out,), "perm_next")
+    if bias is not None:
+        _meta(bias, torch.float32, (d_out,), "bias")
+    wi = torch.empty_like(w_idx)
+    wn = torch.empty_like(w_norm)
+    bo = torch.empty_like(bias) if bias is not None else None
+    _check(lib().oq_fold_permutation(_dev(w_idx, what="w_idx"), _dev(w_norm, what="w_norm"),
+                                     _dev(bias, what="bias") if bias is not None else None, d_out, d_in, bits_w,
+                                     _dev(perm_next, what="perm_next"), _dev(wi, what="w_idx_out"),
+                                     _dev(wn, what="w_norm_out"), _dev(bo, what="bias_out") if bo is not None else None,
+                                     _stream(stream)))
+    return wi, wn, bo
 
 
 def oq_rotate_quantize_act(x, h: int, perm, sign, thresholds, bits_a: int, x_idx=None, s=None,

@@ -151,6 +151,40 @@ oq_status oq_quantize_weights(const void* W, oq_dtype w_dtype, int32_t d_out, in
                               uint8_t* w_idx, float* w_norm, hipStream_t stream);
 
 /*
+ * oq_fold_permutation -- moves the next layer's input permutation into this
+ * layer's output channels (offline).  The RPBH rotation of a layer's input
+ * starts with a uniform random permutation (rcap.io summary, RPBH paragraph;
+ * online pseudo-code).  When the next layer's input is an elementwise
+ * function of this layer's output -- GELU of an MLP's up projection -- the
+ * permutation commutes with that function: with the rows of this layer's
+ * quantized weights, norms and bias reordered as
+ *
+ *   w_idx_out[i] = w_idx[perm_next[i]], w_norm_out[i] = w_norm[perm_next[i]],
+ *   bias_out[i] = bias[perm_next[i]]   (i = 0 .. d_out - 1),
+ *
+ * the layer writes y'[t][i] = y[t][perm_next[i]] bit for bit, and the next
+ * oq_rotate_quantize_act on GELU(y') with perm = identity (perm[i] = i) and
+ * the next layer's own sign table gives the same rotation, indices and norm
+ * as on GELU(y) with (perm_next, sign): its gather reads the staged row in
+ * order.  Nothing is re-quantized.
+ *
+ * w_idx, w_norm : dev, this layer's oq_quantize_weights output ([d_out][d_in *
+ *                 bits_w / 8] bytes, [d_out] float).
+ * bias          : dev [d_out] float or NULL (then bias_out is not written).
+ * d_out         : this layer's output width = the next layer's d_in.
+ * d_in, bits_w  : this layer's; d_in * bits_w / 8 a multiple of 16.
+ * perm_next     : dev [d_out] int32, the next layer's RPBH permutation (from
+ *                 oq_build_rpbh(d_out, h, seed)); entries outside [0, d_out)
+ *                 are clamped, so the copy stays in bounds.
+ * w_idx_out, w_norm_out, bias_out : dev, same shapes, written; they must not
+ *                 overlap the inputs; w_idx and w_idx_out 16-byte aligned.
+ * Errors        : OQ_EINVAL, OQ_EDEVICE.
+ */
+oq_status oq_fold_permutation(const uint8_t* w_idx, const float* w_norm, const float* bias, int32_t d_out,
+                              int32_t d_in, int32_t bits_w, const int32_t* perm_next, uint8_t* w_idx_out,
+                              float* w_norm_out, float* bias_out, hipStream_t stream);
+
+/*
  * oq_rotate_quantize_act -- the online activation step (rcap.io summary,
  * online part of the pseudo-code), per token x: v = R x (fast block Hadamard,
  * O(d log h)), s = |v|, x_idx = q(v / (s + OQ_EPS)).  Hot path.

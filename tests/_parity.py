@@ -22,6 +22,15 @@ REL_GEMM = 2e-3       # relative Frobenius error of the GEMM output
 BAND = 1e-11
 
 
+def sample_rows(T, n, seed=0):
+    """The first and last 16 rows and n random ones (sorted, distinct)."""
+    rng = np.random.default_rng(seed)
+    head = np.arange(min(16, T))
+    tail = np.arange(max(0, T - 16), T)
+    mid = rng.choice(T, size=min(n, T), replace=False)
+    return np.unique(np.concatenate([head, mid, tail]))
+
+
 def log(msg):
     print(msg, flush=True)
     sys.stdout.flush()

@@ -331,12 +331,7 @@ def test_gemm_bf16_output_is_rounded_fp32(T, d, d_out, bits_w, bits_a, gelu):
 # ---- full sizes, sampled outputs ------------------------------------------------
 
 
-def _sample_rows(T, n, seed=0):
-    rng = np.random.default_rng(seed)
-    head = np.arange(min(16, T))
-    tail = np.arange(max(0, T - 16), T)
-    mid = rng.choice(T, size=min(n, T), replace=False)
-    return np.unique(np.concatenate([head, mid, tail]))
+_sample_rows = P.sample_rows
 
 
 def test_full_flux_qkv_w4a4():

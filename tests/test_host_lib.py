@@ -267,3 +267,20 @@ def test_binding_checks_shapes_tables_and_devices_before_calling():
     with pytest.raises(ValueError, match="whole bytes"):
         oq.oq_rotate_quantize_act(torch.zeros((T, 250)), 2, torch.zeros(250, dtype=torch.int32),
                                   torch.zeros(250, dtype=torch.int8), oq.oq_lloyd_max(250, 3)[1], 3)
+
+
+def test_fold_permutation_rejects_invalid_arguments():
+    L = oq.lib()
+    f = _fake()
+    g = _fake((1 << 20) + 4)
+    h = _fake(1 << 24)
+    fo = L.oq_fold_permutation
+    assert fo(f, f, None, 8, 256, 5, f, h, h, None, None) == oq.OQ_EINVAL          # bits_w
+    assert fo(f, f, None, 8, 96, 2, f, h, h, None, None) == oq.OQ_EINVAL           # 24-byte rows
+    assert fo(f, f, None, -1, 256, 4, f, h, h, None, None) == oq.OQ_EINVAL
+    assert fo(None, f, None, 8, 256, 4, f, h, h, None, None) == oq.OQ_EINVAL
+    assert fo(f, f, f, 8, 256, 4, f, h, h, None, None) == oq.OQ_EINVAL             # bias without bias_out
+    assert fo(g, f, None, 8, 256, 4, f, h, h, None, None) == oq.OQ_EINVAL          # alignment
+    assert fo(f, f, None, 8, 256, 4, f, _fake((1 << 20) + 256), h, None, None) == oq.OQ_EINVAL   # overlap
+    assert b"overlap" in L.oq_last_error()
+    assert fo(f, f, None, 0, 256, 4, f, h, h, None, None) == oq.OQ_OK              # no rows

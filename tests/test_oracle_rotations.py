@@ -92,3 +92,23 @@ def test_rotations_agree_without_outliers():
     errs, theory = _errors(x, d, h, bits)
     for k, e in errs.items():
         assert abs(e / theory - 1.0) < 0.05, (k, errs, theory)
+
+
+@pytest.mark.parametrize("d,h", [(256, 64), (1024, 256), (3072, 256)])
+def test_folded_permutation_gives_the_same_rotation(d, h):
+    # R x = B D P x, and P x is x[perm]: a producer whose output channels are
+    # reordered by perm hands over x[perm] directly, and the rotation of it
+    # with the identity permutation and the same signs is the same vector, bit
+    # for bit (the same numbers enter the same butterflies).  The elementwise
+    # GELU between the two layers keeps the order.
+    rng = np.random.default_rng(d + h)
+    perm, sign = rpbh.build_rpbh(d, h, 5)
+    y = rng.standard_normal((7, d)) * 3.0
+    x = quant.gelu_erf(y)
+    folded = quant.gelu_erf(y[:, perm])
+    np.testing.assert_array_equal(folded, x[:, perm])
+    a = rpbh.rotate(x, perm, sign, h)
+    b = rpbh.rotate(folded, np.arange(d), sign, h)
+    np.testing.assert_array_equal(a, b)
+    # and it is not the identity rotation with the same signs on the unfolded vector
+    assert not np.allclose(a, rpbh.rotate(x, np.arange(d), sign, h))
