@@ -185,7 +185,9 @@ oq_status oq_rotate_quantize_act(const void* x, oq_dtype x_dtype, int64_t T, int
   a.g_lo = lo;
   a.g_invw = G > 0 ? G / (hi - lo) : 0.0;
   a.g_rmax = rmax;
+  a.thr_absmax = 0.f;
   for (int i = 0; i < nthr; ++i) {
+    a.thr_absmax = std::fmax(a.thr_absmax, std::fabs(th32[i]));
     a.thr[i] = th32[i];
     a.thr_lo[i] = (float)(thresholds[i] - (double)th32[i]);   // the difference is exact in fp64
   }

@@ -38,6 +38,7 @@ struct RqArgs {
   double g_lo;       // grid origin (u units)
   double g_invw;     // cells per unit u
   double g_rmax;     // widening of each cell for the recheck guard (u units)
+  float thr_absmax;  // max |thr| (the slot-wide guard radius)
   float thr[kMaxThr];
   float thr_lo[kMaxThr];         // threshold - thr, rounded to fp32: thr + thr_lo is the fp64 threshold to 2^-48
   int32_t glut[kHostGrid][2];   // G <= kHostGrid: cell c -> {bits of its threshold (or +inf), thresholds below it}

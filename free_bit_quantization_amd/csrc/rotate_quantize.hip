@@ -432,10 +432,21 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
     }
 
     // ---- 4./5. threshold search and guard ----------------------------------------
+    // Guard radius: the butterfly term of the coordinate's block plus k u
+    // |theta|, with max |theta| for up to 16 levels (one compare per
+    // coordinate) and the compared threshold's own |theta| above; the grid path
+    // notes only whether the lane has a near coordinate, and the flags are
+    // recomputed when some lane does.
     Pack16<BITS> pk;
     uint32_t flags = 0;
     auto put = [&](int r, int idx) { pk.put(r, (uint32_t)idx); };
+    constexpr bool kSlotRadius = BITS <= 4;
+    auto radius = [&](int r, float th) {
+      const float radb = kGam * l1[TWO_PASS ? 0 : r / (16 / BPL)] * c;
+      return kSlotRadius ? fmaf(a.thr_absmax, kRel, radb) : fmaf(fabsf(th), kRel, radb);
+    };
     if (G > 0) {
+      bool near = false;
       // two halves of 8: all LUT reads of a half are in flight together
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
@@ -448,29 +459,35 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
           const int r = 8 * hf + q;
-          const float radb = kGam * l1[TWO_PASS ? 0 : r / (16 / BPL)] * c;
           const float th = __int_as_float(e[q].x);
           const float dd = fmaf(y[r], c, -th);
           put(r, e[q].y + (dd > 0.f ? 1 : 0));
-          flags |= (fabsf(dd) < fmaf(fabsf(th), kRel, radb) ? 1u : 0u) << r;
+          near |= fabsf(dd) < radius(r, th);
+        }
+      }
+      if (__ballot(near && valid) != 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ci = (int)__builtin_amdgcn_fmed3f(fmaf(y[r], cg, og), 0.0f, (float)(G - 1));
+          const float th = __int_as_float(lut[ci].x);
+          flags |= (fabsf(fmaf(y[r], c, -th)) < radius(r, th) ? 1u : 0u) << r;
         }
       }
     } else {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float v = y[r];
-        const float radb = kGam * l1[TWO_PASS ? 0 : r / (16 / BPL)] * c;
         int lo = 0;
         for (int step = 128; step >= 1; step >>= 1)
           if (lo + step <= nthr && fmaf(v, c, -thr[lo + step - 1]) > 0.f) lo += step;
         bool near = false;
         if (lo > 0) {
           const float th = thr[lo - 1];
-          near |= fabsf(fmaf(v, c, -th)) < fmaf(fabsf(th), kRel, radb);
+          near |= fabsf(fmaf(v, c, -th)) < radius(r, th);
         }
         if (lo < nthr) {
           const float th = thr[lo];
-          near |= fabsf(fmaf(v, c, -th)) < fmaf(fabsf(th), kRel, radb);
+          near |= fabsf(fmaf(v, c, -th)) < radius(r, th);
         }
         put(r, lo);
         flags |= (near ? 1u : 0u) << r;
@@ -773,9 +790,19 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
       l1 = group_sum<BL>(l1);
 
       // ---- 4./5. grid search and guard --------------------------------------------
+      // The guard radius: the butterfly term of this slot's block plus k u |theta|
+      // of the threshold compared.  Up to 16 levels one radius covers the slot
+      // (|theta| <= max |theta|: a wider band, hardly more rechecks at these
+      // widths, one compare per coordinate); with more levels each compare uses
+      // its own threshold's term, which keeps the band narrow where rechecks are
+      // frequent.  The fast path only notes whether some coordinate of the lane
+      // is near (a lane mask); the recheck recomputes which.
       const float radb = kGam * l1 * c;
+      const float rad_slot = fmaf(a.thr_absmax, kRel, radb);
+      constexpr bool kSlotRadius = BITS <= 4;
+      auto radius = [&](float th) { return kSlotRadius ? rad_slot : fmaf(fabsf(th), kRel, radb); };
       Pack16<BITS> pw;
-      uint32_t flags = 0;
+      bool near = false;
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         int2 e[8];
@@ -791,7 +818,7 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
           const float dd = fmaf(y[r], c, -th);
           const uint32_t idx = (uint32_t)e[q].y + (dd > 0.f ? 1u : 0u);
           pw.put(r, idx);
-          flags |= (fabsf(dd) < fmaf(fabsf(th), kRel, radb) ? 1u : 0u) << r;
+          near |= fabsf(dd) < radius(th);
         }
       }
 
@@ -799,7 +826,15 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
       // block hold its inputs (pass 1) and its outputs (pass 2), so each group
       // of BL lanes recomputes one of its flagged coordinates per round, all
       // groups at once, with an fp64 sum over the group.
-      if (__ballot(flags != 0) != 0) {
+      if (__ballot(near) != 0) {
+        // which coordinates: the fast path's test again, per coordinate
+        uint32_t flags = 0;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ci = (int)__builtin_amdgcn_fmed3f(fmaf(y[r], cg, og), 0.0f, (float)(G - 1));
+          const float th = __int_as_float(lut[ci].x);
+          flags |= (fabsf(fmaf(y[r], c, -th)) < radius(th) ? 1u : 0u) << r;
+        }
         // the norm again, exactly: fp64 squares of the staged row (sign flips do
         // not change them); the fast path's fp32 partials are only certified.
         // Once per token (8-bit codebooks flag ~2 coordinates per token).

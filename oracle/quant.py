@@ -4,18 +4,18 @@ product, fp64 oracle.
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
 Method ("OrbitQuant: data-agnostic quantization for image and video",
-rcap.io summary, offline and online pseudo-code):
+rcap.io summary, offline and online pseudo-code), in this module's terms:
+with R the orthogonal rotation of input dimension d and c_0 < ... < c_{L-1}
+the levels of the codebook for d,
 
-* weights, offline: W_rot = W @ R.T, row norms n, indices of the nearest
-  centroid of W_rot / n in ``codebook[d, b_w]``; W_hat = diag(n) C[idx];
-* activations, per token: x_rot = x @ R.T, s = ||x_rot||, indices of the
-  nearest centroid of x_rot / (s + eps) in ``codebook[d, b_a]``;
-  x_hat = s C[idx];
-* the rotation cancels inside the layer (W R^T R x = W x, same page,
-  "rotation cancels" paragraph), so the layer output is computed in the
-  rotated basis: y = W_hat x_hat.  The page reports the product itself as
-  a dequantize-then-matmul ("fake quantization", caveats paragraph); the
-  oracle computes exactly that product in fp64.
+* a weight row w (offline) becomes its norm n = |R w| and the index vector
+  q(R w / n), where q(v)_k is the index of the level nearest to v_k;
+* a token x (online) becomes s = |R x| and q(R x / (s + eps));
+* R^T R = I, so R w . R x = w . x (same page, "rotation cancels"
+  paragraph) and the layer output is the dot product of the two dequantized
+  vectors, n c[q_w] . s c[q_x], taken in the rotated basis.  The page
+  measures exactly this as dequantize-then-matmul ("fake quantization",
+  caveats paragraph); here it is computed in fp64.
 
 Readings:
 

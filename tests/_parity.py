@@ -125,9 +125,19 @@ def rotation(d: int, h: int, seed: int = 0, kind: str = "rpbh"):
     return perm, sign, torch.from_numpy(perm).cuda(), torch.from_numpy(sign).cuda()
 
 
+CHUNK = 2048   # oracle rows per pass (bounds host memory at the full workload sizes)
+
+
+def _chunks(rows, n=CHUNK):
+    for i in range(0, len(rows), n):
+        yield rows[i:i + n]
+
+
 def check_activations(x: np.ndarray, dtype: str, h: int, bits: int, seed: int = 0, rows: Optional[np.ndarray] = None,
-                      want_x_rot: bool = True, name: str = "", kind: str = "rpbh"):
-    """rotate-quantize x on the GPU; compare rows (all if None) with the oracle.
+                      want_x_rot: bool = True, name: str = "", kind: str = "rpbh", keep_oracle: bool = False):
+    """rotate-quantize x on the GPU; compare rows (all if None) with the oracle,
+    in chunks of rows.  keep_oracle: the report also carries the oracle's own
+    indices and norms of the checked rows ("_ia", "_s"), for the all-oracle product.
 
     Returns (x_idx device tensor, s device tensor, report dict)."""
     T, d = x.shape
@@ -137,26 +147,43 @@ def check_activations(x: np.ndarray, dtype: str, h: int, bits: int, seed: int = 
     x_idx, s, x_rot = oq.oq_rotate_quantize_act(xd, h, pd, sd, cb.th, bits, want_x_rot=want_x_rot)
     import torch
     torch.cuda.synchronize()
-    rows = np.arange(T) if rows is None else rows
-    xs = np.asarray(xd.float().cpu().numpy(), dtype=np.float64)[rows]
-    ia, s_o, xr_o, u_o = quant.quantize_activations(xs, perm, sign, h, cb.th)
-    gi = quant.unpack(x_idx.cpu().numpy()[rows], bits, d)
-    n, nin, nout = index_mismatches(gi, ia, u_o, cb.th)
-    s_g = s.cpu().numpy()[rows].astype(np.float64)
+    rows = np.arange(T) if rows is None else np.asarray(rows)
+    xi_h = x_idx.cpu().numpy()
+    s_h = s.cpu().numpy()
+    xr_h = x_rot.cpu().numpy() if want_x_rot else None
+    n = nin = nout = 0
+    s_rel = xr_rel = 0.0
+    keep_ia, keep_s = [], []
+    for rc in _chunks(rows):
+        xs = xd[torch.from_numpy(rc).long().cuda()].float().cpu().numpy().astype(np.float64)
+        ia, s_o, xr_o, u_o = quant.quantize_activations(xs, perm, sign, h, cb.th)
+        gi = quant.unpack(xi_h[rc], bits, d)
+        m = index_mismatches(gi, ia, u_o, cb.th)
+        n, nin, nout = n + m[0], nin + m[1], nout + m[2]
+        s_rel = max(s_rel, float(np.max(np.abs(s_h[rc].astype(np.float64) - s_o) / np.maximum(s_o, 1e-30))))
+        if want_x_rot:
+            num = np.linalg.norm(xr_h[rc].astype(np.float64) - xr_o, axis=1)
+            den = np.maximum(np.linalg.norm(xr_o, axis=1), 1e-30)
+            xr_rel = max(xr_rel, float(np.max(num / den)))
+        if keep_oracle:
+            keep_ia.append(ia.astype(np.uint8))
+            keep_s.append(s_o)
+        del ia, s_o, xr_o, u_o, xs
     rep = {"name": name, "T": T, "d": d, "h": h, "bits": bits, "checked_rows": len(rows),
-           "idx_mismatch": n, "idx_in_band": nin, "idx_out_of_band": nout,
-           "s_rel": float(np.max(np.abs(s_g - s_o) / np.maximum(s_o, 1e-30)))}
+           "idx_mismatch": n, "idx_in_band": nin, "idx_out_of_band": nout, "s_rel": s_rel}
     if want_x_rot:
-        xr_g = x_rot.cpu().numpy()[rows].astype(np.float64)
-        num = np.linalg.norm(xr_g - xr_o, axis=1)
-        den = np.maximum(np.linalg.norm(xr_o, axis=1), 1e-30)
-        rep["x_rot_rel"] = float(np.max(num / den))
+        rep["x_rot_rel"] = xr_rel
     log(f"[act] {rep}")
+    if keep_oracle:
+        rep["_ia"] = np.concatenate(keep_ia)
+        rep["_s"] = np.concatenate(keep_s)
+        rep["_rows"] = rows
     return x_idx, s, rep
 
 
 def check_weights(W: np.ndarray, h: int, bits: int, seed: int = 0, name: str = "", kind: str = "rpbh"):
-    """Quantize W on the GPU (fp64 path); indices must be bit-exact."""
+    """Quantize W on the GPU (fp64 path); indices must be bit-exact.  The
+    report carries the oracle's indices and norms ("_iw", "_n")."""
     d_out, d = W.shape
     perm, sign, pd, sd = rotation(d, h, seed, kind)
     cb = library_codebook(d, bits)
@@ -168,6 +195,8 @@ def check_weights(W: np.ndarray, h: int, bits: int, seed: int = 0, name: str = "
     nrel = float(np.max(np.abs(w_norm.cpu().numpy() - n_o) / n_o))
     rep = {"name": name, "d_out": d_out, "d": d, "bits": bits, "idx_mismatch": n, "w_norm_rel": nrel}
     log(f"[w] {rep}")
+    rep["_iw"] = iw.astype(np.uint8)
+    rep["_n"] = n_o
     return w_idx, w_norm, rep
 
 
@@ -185,31 +214,73 @@ def run_gemm(x_idx, s, w_idx, w_norm, d, bits_a, bits_w, ca, cw, bias=None, epil
 
 
 def check_gemm(x_idx, s, w_idx, w_norm, d: int, bits_a: int, bits_w: int, bias=None, gelu=False,
-               rows: Optional[np.ndarray] = None, name: str = "", out_dtype=None, split=False, workspace=None):
-    """GEMM on the GPU vs the oracle's dequantized product of the GPU's own indices.
+               rows: Optional[np.ndarray] = None, name: str = "", out_dtype=None, split=False, workspace=None,
+               all_oracle=None):
+    """GEMM on the GPU vs the oracle's dequantized product of the GPU's own
+    indices, s and norms (rows: all if None), in chunks of rows.
 
     split=True runs oq_qlinear_splitk (stream-K tail through a workspace).
+    all_oracle = (act report, weight report) with the oracle's own indices:
+    the error against the all-oracle product is reported too (information).
     With out_dtype=torch.bfloat16 the GEMM also runs with bf16 output; that
     tensor must hold the fp32 output rounded to nearest even, bit for bit
     (report key "bf16_equal"), and it is the one returned."""
     import torch
     ca = library_codebook(d, bits_a)
     cw = library_codebook(d, bits_w)
-    bd = None if bias is None else torch.from_numpy(bias).cuda()
+    bd = None if bias is None else torch.from_numpy(np.asarray(bias, dtype=np.float32)).cuda()
     epi = oq.OQ_EPI_GELU_ERF if gelu else oq.OQ_EPI_NONE
     y = run_gemm(x_idx, s, w_idx, w_norm, d, bits_a, bits_w, ca.c, cw.c, bias=bd, epilogue=epi, split=split,
                  workspace=workspace)
     torch.cuda.synchronize()
     T = s.shape[0]
-    rows = np.arange(T) if rows is None else rows
-    ia = quant.unpack(x_idx.cpu().numpy()[rows], bits_a, d)
+    rows = np.arange(T) if rows is None else np.asarray(rows)
     iw = quant.unpack(w_idx.cpu().numpy(), bits_w, d)
-    ref = quant.dequantized_product(ia, s.cpu().numpy()[rows], iw, w_norm.cpu().numpy(), ca.c, cw.c,
-                                    bias=bias, gelu=gelu)
-    yg = y.cpu().numpy()[rows]
-    err = rel_frob(yg, ref)
-    rep = {"name": name, "split": split, "T": T, "N": w_norm.shape[0], "K": d, "checked_rows": len(rows), "rel_frob": err,
-           "tile_rel_max": tile_rel_max(yg, ref, rows), "finite": bool(np.all(np.isfinite(yg)))}
+    nw = w_norm.cpu().numpy()
+    xi_h = x_idx.cpu().numpy()
+    s_h = s.cpu().numpy()
+    bias_h = None if bias is None else np.asarray(bias, dtype=np.float64)
+    num2 = den2 = 0.0
+    tiles = {}
+    finite = True
+    a_num2 = a_den2 = 0.0
+    if all_oracle is not None:
+        ra, rw = all_oracle
+        pos = {int(r): i for i, r in enumerate(ra["_rows"])}
+    for rc in _chunks(rows):
+        ia = quant.unpack(xi_h[rc], bits_a, d)
+        ref = quant.dequantized_product(ia, s_h[rc], iw, nw, ca.c, cw.c, bias=bias_h, gelu=gelu)
+        yg = y[torch.from_numpy(rc).long().cuda()].float().cpu().numpy().astype(np.float64)
+        finite &= bool(np.all(np.isfinite(yg)))
+        diff2 = (yg - ref) ** 2
+        num2 += float(diff2.sum())
+        den2 += float((ref ** 2).sum())
+        rb = rc // 256
+        for b in np.unique(rb):
+            sel = rb == b
+            for c0 in range(0, ref.shape[1], 256):
+                key = (int(b), c0)
+                t = tiles.setdefault(key, [0.0, 0.0])
+                t[0] += float(diff2[sel, c0:c0 + 256].sum())
+                t[1] += float((ref[sel, c0:c0 + 256] ** 2).sum())
+        if all_oracle is not None:
+            idx = np.array([pos[int(r)] for r in rc])
+            ref_o = quant.dequantized_product(ra["_ia"][idx], ra["_s"][idx], rw["_iw"], rw["_n"], ca.c, cw.c,
+                                              bias=bias_h, gelu=gelu)
+            a_num2 += float(((yg - ref_o) ** 2).sum())
+            a_den2 += float((ref_o ** 2).sum())
+        del ia, ref, yg, diff2
+    worst = 0.0
+    for n2, d2 in tiles.values():
+        if d2 > 0:
+            worst = max(worst, float(np.sqrt(n2 / d2)))
+        elif n2 > 0:
+            worst = float("inf")
+    err = float(np.sqrt(num2 / max(den2, 1e-300)))
+    rep = {"name": name, "split": split, "T": T, "N": w_norm.shape[0], "K": d, "checked_rows": len(rows),
+           "rel_frob": err, "tile_rel_max": worst, "finite": finite}
+    if all_oracle is not None:
+        rep["rel_frob_vs_all_oracle"] = float(np.sqrt(a_num2 / max(a_den2, 1e-300)))
     if out_dtype is not None:
         y16 = run_gemm(x_idx, s, w_idx, w_norm, d, bits_a, bits_w, ca.c, cw.c, bias=bd, epilogue=epi, split=split,
                        out_dtype=out_dtype, workspace=workspace)

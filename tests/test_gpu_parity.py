@@ -44,19 +44,27 @@ def _assert_gemm(rep):
 
 
 def run_linear(lin, index=0, T=None, seed=0, bias=False, act_rows=None, gemm_rows=None, x=None, W_=None,
-               x_dtype=None, kind="rpbh", out_dtype=None):
+               x_dtype=None, kind="rpbh", out_dtype=None, split=False):
+    """One linear through the GPU path against the oracle: every checked
+    activation row and GEMM row (all rows when act_rows / gemm_rows are None).
+    The GEMM's error against the all-oracle product (the oracle's own indices,
+    norms and scales) is reported as information when the GEMM rows are a
+    subset of the checked activation rows."""
     P.log(f"== linear {lin.name} T={T or lin.T} K={lin.d_in} N={lin.d_out} W{lin.bits_w}A{lin.bits_a}")
     xg, Wg = synth.gen_linear(lin, seed, index, T=T, need_act=x is None)
     x = xg if x is None else x
     W_ = Wg if W_ is None else W_
     x_idx, s, ra = P.check_activations(x, x_dtype or lin.act_dtype, lin.h, lin.bits_a, rows=act_rows,
-                                       want_x_rot=True, name=lin.name, kind=kind)
+                                       want_x_rot=True, name=lin.name, kind=kind, keep_oracle=True)
     _assert_act(ra)
     w_idx, w_norm, rw = P.check_weights(W_, lin.h, lin.bits_w, name=lin.name, kind=kind)
     _assert_w(rw)
     b = synth.gen_bias(lin.d_out, seed) if bias else None
+    rows_g = np.arange(x.shape[0]) if gemm_rows is None else np.asarray(gemm_rows)
+    both = set(rows_g.tolist()) <= set(ra["_rows"].tolist())
     y, rg = P.check_gemm(x_idx, s, w_idx, w_norm, lin.d_in, lin.bits_a, lin.bits_w, bias=b,
-                         gelu=lin.epilogue == "gelu", rows=gemm_rows, name=lin.name, out_dtype=out_dtype)
+                         gelu=lin.epilogue == "gelu", rows=gemm_rows, name=lin.name, out_dtype=out_dtype,
+                         split=split, all_oracle=(ra, rw) if both else None)
     _assert_gemm(rg)
     if out_dtype is not None:
         assert rg["bf16_equal"], rg
@@ -334,39 +342,175 @@ def test_gemm_bf16_output_is_rounded_fp32(T, d, d_out, bits_w, bits_a, gelu):
 _sample_rows = P.sample_rows
 
 
+# every token of every linear; the oracle works through the rows in chunks
+
+
 def test_full_flux_qkv_w4a4():
-    lin = W["flux_qkv_w4a4"].linears[0]
-    run_linear(lin, act_rows=None, gemm_rows=_sample_rows(lin.T, 96))
+    run_linear(W["flux_qkv_w4a4"].linears[0])
 
 
 def test_full_flux_mlp_w2a4_chain():
+    # the down projection takes the GPU's own GELU output; the whole chain
+    # against the all-oracle chain (the oracle's indices everywhere) is reported
     up, down = W["flux_mlp_w2a4"].linears
-    rows = _sample_rows(up.T, 64)
-    y_up = run_linear(up, index=0, act_rows=_sample_rows(up.T, 512), gemm_rows=rows)
+    y_up = run_linear(up, index=0)
     x_down = y_up.cpu().numpy()
     _, W_down = synth.gen_linear(down, 0, 1, T=1, need_act=False)
-    run_linear(down, index=1, x=x_down, W_=W_down, x_dtype="f32", act_rows=_sample_rows(down.T, 512),
-               gemm_rows=rows)
+    y = run_linear(down, index=1, x=x_down, W_=W_down, x_dtype="f32")
+    _chain_against_all_oracle(up, down, W_down, y)
+
+
+def _chain_against_all_oracle(up, down, W_down, y, nrows=128):
+    from oracle import quant
+    rows = P.sample_rows(up.T, nrows)
+    x, W_up = synth.gen_linear(up, 0, 0)
+    pu, su, _, _ = P.rotation(up.d_in, up.h, 0)
+    pdn, sdn, _, _ = P.rotation(down.d_in, down.h, 0)
+    ca, cw = P.library_codebook(up.d_in, up.bits_a), P.library_codebook(up.d_in, up.bits_w)
+    cda, cdw = P.library_codebook(down.d_in, down.bits_a), P.library_codebook(down.d_in, down.bits_w)
+    ia, s_a, _, _ = quant.quantize_activations(x.astype(np.float64)[rows], pu, su, up.h, ca.th)
+    iw, n_w, _, _ = quant.quantize_weights(W_up.astype(np.float64), pu, su, up.h, cw.th)
+    h = quant.dequantized_product(ia, s_a, iw, n_w, ca.c, cw.c, gelu=True)
+    ia2, s2, _, _ = quant.quantize_activations(h, pdn, sdn, down.h, cda.th)
+    iw2, n2, _, _ = quant.quantize_weights(W_down.astype(np.float64), pdn, sdn, down.h, cdw.th)
+    y_o = quant.dequantized_product(ia2, s2, iw2, n2, cda.c, cdw.c)
+    err = P.rel_frob(y.float().cpu().numpy()[rows], y_o)
+    P.log(f"[chain] GPU chain vs all-oracle chain: rel Frobenius {err:.3e} over {len(rows)} rows (information)")
+    assert np.isfinite(err) and err <= 2e-2, err
 
 
 def test_full_flux_mlp_w2a4_chain_bf16_hidden():
     up, down = W["flux_mlp_w2a4"].linears
-    rows = _sample_rows(up.T, 64)
-    h16 = run_linear(up, index=0, act_rows=_sample_rows(up.T, 256), gemm_rows=rows, out_dtype=torch.bfloat16)
+    h16 = run_linear(up, index=0, out_dtype=torch.bfloat16)
     x_down = h16.float().cpu().numpy()
     _, W_down = synth.gen_linear(down, 0, 1, T=1, need_act=False)
-    run_linear(down, index=1, x=x_down, W_=W_down, x_dtype="bf16", act_rows=_sample_rows(down.T, 256),
-               gemm_rows=rows)
+    run_linear(down, index=1, x=x_down, W_=W_down, x_dtype="bf16")
 
 
 def test_full_wan_ffn_w4a4():
-    lin = W["wan_ffn_w4a4"].linears[0]
-    run_linear(lin, act_rows=_sample_rows(lin.T, 1024), gemm_rows=_sample_rows(lin.T, 48))
+    run_linear(W["wan_ffn_w4a4"].linears[0])
 
 
-def test_full_flux_block_w4a8():
-    for k, lin in enumerate(W["flux_block_w4a8_b2"].linears):
-        run_linear(lin, index=k, act_rows=_sample_rows(lin.T, 256), gemm_rows=_sample_rows(lin.T, 32))
+@pytest.mark.parametrize("k", range(8))
+def test_full_flux_block_w4a8(k):
+    run_linear(W["flux_block_w4a8_b2"].linears[k], index=k)
+
+
+def test_full_flux_qkv_split_every_tile():
+    # the split entry point on the full FLUX QKV shape (the plan decides
+    # whether the last round is split), every output row checked
+    run_linear(W["flux_qkv_w4a4"].linears[0], split=True)
+
+
+# ---- the GELU epilogue against fp64 GELU of the GPU's own pre-activation -------
+
+
+@pytest.mark.parametrize("T,d,n,bits_w,bits_a,split", [(300, 1024, 520, 2, 4, False), (4608, 3072, 1024, 2, 4, True),
+                                                       (129, 3072, 517, 4, 8, False)])
+def test_gelu_epilogue_matches_fp64_gelu_of_the_gpu_output(T, d, n, bits_w, bits_a, split):
+    # the same inputs through the GEMM with and without the GELU epilogue:
+    # GELU_fp64(y_none) must equal y_gelu to 1e-6 relative (absolute floor
+    # 1e-6 * max|y| near zero, where GELU(y) ~ y / 2 carries y's rounding)
+    from free_bit_quantization_amd import oq
+    from oracle import quant
+    lin = synth.Linear(f"gelu-{T}", T, d, n, 256, bits_w, bits_a, "student_t", "bf16", 10, 30.0, 0.5, 5, 10.0)
+    x, Wm = synth.gen_linear(lin, 4, 0)
+    x_idx, s, _ = P.check_activations(x, "bf16", 256, bits_a, rows=np.arange(4), want_x_rot=False)
+    w_idx, w_norm, _ = P.check_weights(Wm, 256, bits_w)
+    ca, cw = P.library_codebook(d, bits_a), P.library_codebook(d, bits_w)
+    bias = torch.from_numpy(synth.gen_bias(n, 2)).cuda()
+    y0 = P.run_gemm(x_idx, s, w_idx, w_norm, d, bits_a, bits_w, ca.c, cw.c, bias=bias, split=split,
+                    workspace=oq.qlinear_workspace(T, n, d, bits_a, bits_w) if split else None)
+    y1 = P.run_gemm(x_idx, s, w_idx, w_norm, d, bits_a, bits_w, ca.c, cw.c, bias=bias, epilogue=oq.OQ_EPI_GELU_ERF,
+                    split=split, workspace=oq.qlinear_workspace(T, n, d, bits_a, bits_w) if split else None)
+    torch.cuda.synchronize()
+    g = quant.gelu_erf(y0.cpu().numpy().astype(np.float64))
+    got = y1.cpu().numpy().astype(np.float64)
+    floor = 1e-6 * float(np.max(np.abs(g)))
+    rel = np.abs(got - g) / np.maximum(np.abs(g), floor)
+    P.log(f"[gelu] max relative difference {rel.max():.3e} over {got.size} outputs")
+    assert rel.max() <= 1e-6
+
+
+# ---- launch geometry: the result does not depend on how the launch is cut --------
+
+
+def test_rotate_quantize_launch_geometry_invariance():
+    # 4096 tokens run with 12 wavefronts per workgroup, 2048 tokens with 8
+    # (the plan switches at 3072): the rows they share are bit-identical, as
+    # are 100 tokens (fewer tokens than workgroups)
+    from free_bit_quantization_amd import oq
+    lin = W["flux_qkv_w4a4"].linears[0]
+    x, _ = synth.gen_linear(lin, 2, 0, T=4096)
+    perm, sign, pd, sd = P.rotation(3072, 256, 0)
+    for bits in (4, 8):
+        th = P.library_codebook(3072, bits).th
+        xd = P.to_device(x, "bf16")
+        outs = [oq.oq_rotate_quantize_act(xd[:n].contiguous(), 256, pd, sd, th, bits, want_x_rot=True)
+                for n in (4096, 2048, 100)]
+        torch.cuda.synchronize()
+        for (xi, s_, xr), n in zip(outs[1:], (2048, 100)):
+            assert torch.equal(xi, outs[0][0][:n]) and torch.equal(s_, outs[0][1][:n])
+            assert torch.equal(xr, outs[0][2][:n])
+
+
+def test_gemm_launch_geometry_invariance():
+    # the same rows in a launch of 18 x 36 tiles and of 2 x 36 tiles (other
+    # grid, other tile-to-workgroup map): bit-identical whole-tile outputs
+    lin = W["flux_qkv_w4a4"].linears[0]
+    x, Wm = synth.gen_linear(lin, 6, 0)
+    x_idx, s, _ = P.check_activations(x, "bf16", 256, 4, rows=np.arange(4), want_x_rot=False)
+    w_idx, w_norm, _ = P.check_weights(Wm, 256, 4)
+    cb = P.library_codebook(3072, 4)
+    y_all = P.run_gemm(x_idx, s, w_idx, w_norm, 3072, 4, 4, cb.c, cb.c)
+    y_few = P.run_gemm(x_idx[:512].contiguous(), s[:512].contiguous(), w_idx, w_norm, 3072, 4, 4, cb.c, cb.c)
+    torch.cuda.synchronize()
+    assert torch.equal(y_all[:512], y_few)
+
+
+# ---- the workgroup kernel's binary search (no search grid fits) ------------------
+
+
+@pytest.mark.parametrize("d,h,dtype", [(1024, 256, "bf16"), (12288, 256, "f32"), (256, 16, "f32")])
+def test_rotate_quantize_binary_search_without_grid(d, h, dtype):
+    # thresholds with two of them closer than the guard band allows for a
+    # grid cell: the host builds no grid, and the workgroup kernel searches
+    # the thresholds by bisection (the path with G = 0), still certified
+    from free_bit_quantization_amd import oq
+    from oracle import quant
+    rng = np.random.default_rng(d + 1)
+    th = P.library_codebook(d, 4).th.copy()
+    th[9] = th[8] * (1.0 + 3e-6)          # a gap of 3e-6 relative: below 2.2 guard radii
+    assert np.all(np.diff(th) > 0) and np.all(np.diff(th.astype(np.float32)) > 0)
+    perm, sign, pd, sd = P.rotation(d, h, 0)
+    x = rng.standard_t(3, size=(70, d)).astype(np.float32)
+    # a quarter of the coordinates near the close pair, in the rotated basis
+    from oracle import rpbh
+    z = rpbh.rotate(x.astype(np.float64), perm, sign, h)
+    nrm = np.linalg.norm(z, axis=1, keepdims=True)
+    mask = rng.random(z.shape) < 0.1
+    zm = th[8] * nrm * (1.0 + rng.choice([-1e-6, 1e-6, 2e-6, 4e-6], z.shape))
+    # rescale the other coordinates so the row keeps its norm: the placed
+    # coordinates then sit at u = th[8] (1 + e) up to the input's rounding
+    rest2 = np.sum(np.where(mask, 0.0, z) ** 2, axis=1, keepdims=True)
+    alpha = np.sqrt((nrm ** 2 - np.sum(np.where(mask, zm, 0.0) ** 2, axis=1, keepdims=True)) / rest2)
+    z = np.where(mask, zm, alpha * z)
+    xb = rpbh.rotate(z, np.arange(d), np.ones(d, dtype=np.int8), h)
+    x2 = np.empty_like(xb)
+    x2[:, perm] = sign[None, :] * xb
+    x2 = x2.astype(np.float32)
+    if dtype == "bf16":
+        x2 = synth.bf16_round(x2)
+    xd = P.to_device(x2, dtype)
+    xi, s_, _ = oq.oq_rotate_quantize_act(xd, h, pd, sd, th, 4)
+    torch.cuda.synchronize()
+    ia, s_o, _, u_o = quant.quantize_activations(xd.float().cpu().numpy().astype(np.float64), perm, sign, h, th)
+    gi = quant.unpack(xi.cpu().numpy(), 4, d)
+    n, nin, nout = P.index_mismatches(gi, ia, u_o, th)
+    near = np.min(np.abs(u_o[:, :, None] - th[None, None, 8:10]), axis=2) < (1e-4 if dtype == "f32" else 3e-2) * th[8]
+    P.log(f"[bisect] d={d} {dtype}: mismatches {n} in band {nin} out of band {nout}; {int(near.sum())} near the pair")
+    assert nout == 0 and near.sum() > 0
+    assert np.max(np.abs(s_.cpu().numpy() - s_o) / s_o) <= P.REL_S
 
 
 # ---- the certified guard under pressure: coordinates placed at the thresholds ----
