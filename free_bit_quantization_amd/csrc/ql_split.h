@@ -49,11 +49,10 @@ struct QlSplit {
   int32_t classes;   // workgroup classes (1 or 8)
 };
 
-// The plan: split the tail when a workspace with at least `slots` partial-tile
-// slots is available (slots >= the workgroup count), the tail holds at least 8
-// tiles, a tile has at least 4 stages and the tail would otherwise leave more
-// than a fifth of the `cus` workgroups idle.
-OQ_HD inline QlSplit ql_split_plan(int64_t ntiles, int32_t nst, int32_t cus, int64_t slots) {
+// The split of a launch whose tail (the last ntiles % cus tiles) is cut along K
+// when `split` holds (needs nst >= 2, so that a run of lmin stages never spans
+// more than two tiles); otherwise whole tiles only.
+OQ_HD inline QlSplit ql_split_make(int64_t ntiles, int32_t nst, int32_t cus, bool split) {
   QlSplit p;
   p.ntiles = ntiles;
   p.nst = nst;
@@ -63,7 +62,7 @@ OQ_HD inline QlSplit ql_split_plan(int64_t ntiles, int32_t nst, int32_t cus, int
   p.classes = 1;
   p.grid = (int32_t)(ntiles < cus ? ntiles : cus);
   const int64_t full = ntiles / cus, rem = ntiles % cus;
-  if (slots >= cus && rem >= 8 && nst >= 4 && rem * 5 < (int64_t)cus * 4) {
+  if (split && rem > 0 && nst >= 2) {
     p.grid = cus;
     p.n_dp = full * cus;
     p.sk_tiles = (int32_t)rem;
@@ -71,6 +70,25 @@ OQ_HD inline QlSplit ql_split_plan(int64_t ntiles, int32_t nst, int32_t cus, int
     p.classes = cus % 8 == 0 ? 8 : 1;
   }
   return p;
+}
+
+// When the split pays (measured on MI355X, 256 CUs, with HIP events over
+// whole-tile and split launches of the same shapes): a split tile costs its
+// partial tiles' round trip through memory and a finisher's wait, so it wins
+// when the whole-tile tail would leave most CUs idle.  At 24 stages per tile
+// it won for tails up to ~a quarter of the CUs (+16 % at 36 tiles, +4 % at 24)
+// and lost beyond (-5 % at 104 and 136 tiles, -14 % at 216); at 96 and 192
+// stages it won up to three quarters (+130 % at 24 tiles, +9 % at 144, +2 % at
+// 192) and lost above (-2 % at 216, -4 % at 240).
+OQ_HD inline bool ql_split_pays(int64_t rem, int32_t nst, int32_t cus) {
+  if (rem <= 0 || nst < 4) return false;
+  return rem * 4 <= cus || (nst >= 64 && rem * 4 <= (int64_t)cus * 3);
+}
+
+// The plan: split the tail when a workspace with at least `slots` partial-tile
+// slots is available (slots >= the workgroup count) and the split pays.
+OQ_HD inline QlSplit ql_split_plan(int64_t ntiles, int32_t nst, int32_t cus, int64_t slots) {
+  return ql_split_make(ntiles, nst, cus, slots >= cus && ql_split_pays(cus > 0 ? ntiles % cus : 0, nst, cus));
 }
 
 // ---- whole tiles -----------------------------------------------------------

@@ -13,8 +13,9 @@
 //   6. a workgroup leaves at most one partial (one slot per workgroup), and
 //      computes it before any piece it finishes;
 //   7. the grid fits the workspace's slots.
-// Usage: ql_split_check ntiles nst cus [slots]   (one case)
-//        ql_split_check sweep                      (a broad sweep)
+// Usage: ql_split_check ntiles nst cus [slots]   (one case, the plan's choice)
+//        ql_split_check sweep                      (a broad sweep: the plan, and
+//                                                   the split forced on every tail)
 // Prints "ok <cases>" or the first violated invariant, exit status 1.
 #include <cstdio>
 #include <cstdlib>
@@ -33,8 +34,14 @@ static int fail(const char* what, int64_t ntiles, int nst, int cus, int64_t slot
   return 1;
 }
 
+static int check_split(const QlSplit& p, int64_t ntiles, int nst, int cus, int64_t slots);
+
+// the plan for a workspace of `slots` slots
 static int check(int64_t ntiles, int nst, int cus, int64_t slots) {
-  const QlSplit p = ql_split_plan(ntiles, nst, cus, slots);
+  return check_split(ql_split_plan(ntiles, nst, cus, slots), ntiles, nst, cus, slots);
+}
+
+static int check_split(const QlSplit& p, int64_t ntiles, int nst, int cus, int64_t slots) {
   if (p.grid <= 0 || p.grid > cus) return fail("grid", ntiles, nst, cus, slots, p.grid);
   if (p.n_dp + p.sk_tiles != ntiles) return fail("tile count", ntiles, nst, cus, slots, (long)p.n_dp, p.sk_tiles);
   if (p.sk_tiles > 0 && p.grid > slots) return fail("slots", ntiles, nst, cus, slots, p.grid);
@@ -125,6 +132,11 @@ int main(int argc, char** argv) {
         for (int64_t nt = 1; nt <= 3 * cus + 9; ++nt) {
           for (int64_t slots : {(int64_t)0, (int64_t)cus, (int64_t)cus - 1}) {
             if (check(nt, nst, cus, slots)) return 1;
+            ++cases;
+          }
+          // the split mechanism on every tail, whatever the plan would choose
+          if (nst >= 2 && nt % cus != 0) {
+            if (check_split(ql_split_make(nt, nst, cus, true), nt, nst, cus, cus)) return 1;
             ++cases;
           }
         }

@@ -272,24 +272,29 @@ def test_stream_k_split_tiles(T, d, d_out, bits_w, bits_a):
     _gemm_twice(lin, np.arange(T), seed=T + d, bias=ragged, gelu=ragged)
 
 
-def test_flux_qkv_last_round_tiles_twice():
-    # 648 tiles on 256 CUs: two whole rounds, then the last 136 tiles (M rows
-    # 3072 .. 4607 in the grouped raster order) split by K stages, 17 per
-    # class; checked tile by tile on two launches in a row; the first two
-    # rounds bit-identical to the whole-tile entry point
-    lin = W["flux_qkv_w4a4"].linears[0]
-    y_split, y_whole = _gemm_twice(lin, np.arange(3072, lin.T), seed=5)
-    assert _untouched_tiles_equal(y_split, y_whole, lin.T, lin.d_out, 512) == 3072
+@pytest.mark.parametrize("T,d,d_out,bits_w,bits_a,rows0,n_dp", [
+    (2048, 3072, 9216, 4, 4, 1024, 256),     # 288 tiles: one whole round, 32 tiles of 24 stages split
+    (8192, 12288, 3072, 4, 8, 5120, 256)])   # 384 tiles: one whole round, 128 tiles of 192 stages split
+def test_last_round_split_after_whole_rounds_twice(T, d, d_out, bits_w, bits_a, rows0, n_dp):
+    # more tiles than CUs: the first round whole, the tail split by K stages;
+    # the tail's rows (grouped raster order, 4 block rows at a time) checked
+    # tile by tile on two launches in a row, the rows before it bit-identical
+    # to the whole-tile entry point
+    lin = synth.Linear(f"tail-{T}x{d}x{d_out}", T, d, d_out, 256, bits_w, bits_a, "student_t", "bf16", 10, 30.0,
+                       0.5, 5, 10.0)
+    y_split, y_whole = _gemm_twice(lin, np.arange(rows0, T), seed=5)
+    assert _untouched_tiles_equal(y_split, y_whole, T, d_out, n_dp) == rows0
 
 
 def test_split_workspace_size_and_rejection():
     from free_bit_quantization_amd import oq
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    n = oq.oq_qlinear_workspace_size(4608, 9216, 3072, 4, 4)
+    n = oq.oq_qlinear_workspace_size(2048, 9216, 3072, 4, 4)              # 288 tiles: a tail of 32 split
     slots_off = 256 + ((4 * cus + 255) // 256) * 256
     assert n == slots_off + cus * 256 * 256 * 4, (n, cus)
-    assert oq.oq_qlinear_workspace_size(256, 256, 3072, 4, 4) == 0       # one tile: no split
-    assert oq.oq_qlinear_workspace_size(4608, 1024, 3072, 4, 4) == n     # 72 tiles: split
+    assert oq.oq_qlinear_workspace_size(4608, 9216, 3072, 4, 4) == 0     # a tail of 136 short tiles: whole
+    assert oq.oq_qlinear_workspace_size(256, 256, 256, 4, 4) == 0        # 2 K stages: no split
+    assert oq.oq_qlinear_workspace_size(256, 256, 3072, 4, 4) == n       # one tile of 24 stages: split
     lin = synth.Linear("ws", 512, 1024, 1024, 256, 4, 4, "student_t", "bf16", 10, 30.0, 0.5, 5, 10.0)
     x, Wm = synth.gen_linear(lin, 1, 0)
     x_idx, s, _ = P.check_activations(x, "bf16", 256, 4, rows=np.arange(4), want_x_rot=False)
@@ -303,9 +308,16 @@ def test_split_workspace_size_and_rejection():
     assert e.value.status == oq.OQ_EINVAL and "workspace" in str(e.value)
     with pytest.raises(oq.OQError):
         oq.oq_qlinear_splitk(x_idx, s, w_idx, w_norm, 1024, cb.c, 4, cb.c, 4, None)
-    # a shape without a split ignores the workspace
-    y = oq.oq_qlinear_splitk(x_idx[:1], s[:1], w_idx[:256], w_norm[:256], 1024, cb.c, 4, cb.c, 4, None)
-    y0 = oq.oq_qlinear(x_idx[:1], s[:1], w_idx[:256], w_norm[:256], 1024, cb.c, 4, cb.c, 4)
+    # a shape without a split (2 K stages per tile) ignores the workspace
+    g = torch.Generator(device="cuda").manual_seed(3)
+    xi2 = torch.randint(0, 256, (300, 128), dtype=torch.uint8, device="cuda", generator=g)
+    wi2 = torch.randint(0, 256, (300, 128), dtype=torch.uint8, device="cuda", generator=g)
+    s2 = torch.rand(300, device="cuda", generator=g) + 0.5
+    n2 = torch.rand(300, device="cuda", generator=g) + 0.5
+    cb2 = P.library_codebook(256, 4)
+    assert oq.oq_qlinear_workspace_size(300, 300, 256, 4, 4) == 0
+    y = oq.oq_qlinear_splitk(xi2, s2, wi2, n2, 256, cb2.c, 4, cb2.c, 4, None)
+    y0 = oq.oq_qlinear(xi2, s2, wi2, n2, 256, cb2.c, 4, cb2.c, 4)
     torch.cuda.synchronize()
     assert torch.equal(y, y0)
 
@@ -397,8 +409,8 @@ def test_full_flux_block_w4a8(k):
 
 
 def test_full_flux_qkv_split_every_tile():
-    # the split entry point on the full FLUX QKV shape (the plan decides
-    # whether the last round is split), every output row checked
+    # the split entry point on the full FLUX QKV shape (its plan takes whole
+    # tiles: a tail of 136 tiles of 24 stages), every output row checked
     run_linear(W["flux_qkv_w4a4"].linears[0], split=True)
 
 

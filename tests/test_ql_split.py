@@ -65,15 +65,24 @@ def test_split_of_workload_shapes(checker, T, K, N, bits_a, cus):
     _run(checker, _tiles(T, N), _stages(K, bits_a), cus)
 
 
-def test_flux_qkv_takes_the_split_on_256_cus(checker):
+def test_plan_follows_the_measured_split_gains(checker):
+    # FLUX QKV: 648 tiles of 24 stages, a tail of 136 tiles: the split lost
+    # 4.5 %, so whole tiles; the MLP down projection at 1024 tokens (48 tiles of
+    # 96 stages) gained 109 % from the split; 288 tiles of 24 stages (a tail of
+    # 32) gained 9 %; 216 tiles of 96 stages lost 2 %
     out = _run(checker, _tiles(4608, 9216), _stages(3072, 4), 256)
-    # 648 tiles: two whole rounds, the last 136 tiles split along K, 8 classes
-    assert "n_dp=512 sk_tiles=136 grid=256 classes=8" in out, out
+    assert "n_dp=648 sk_tiles=0 grid=256" in out, out
+    out = _run(checker, _tiles(1024, 3072), _stages(12288, 4), 256)
+    assert "n_dp=0 sk_tiles=48 grid=256 classes=8" in out, out
+    out = _run(checker, _tiles(2048, 9216), _stages(3072, 4), 256)
+    assert "n_dp=256 sk_tiles=32 grid=256 classes=8" in out, out
+    out = _run(checker, _tiles(4608, 3072), _stages(12288, 4), 256)
+    assert "n_dp=216 sk_tiles=0" in out, out
 
 
 def test_no_split_without_slots(checker):
-    out = _run(checker, _tiles(4608, 9216), _stages(3072, 4), 256, 0)
-    assert "n_dp=648 sk_tiles=0 grid=256" in out, out
+    out = _run(checker, _tiles(1024, 3072), _stages(12288, 4), 256, 0)
+    assert "n_dp=48 sk_tiles=0 grid=48" in out, out
 
 
 def test_sweep_of_tile_counts_stages_and_cu_counts(checker):
