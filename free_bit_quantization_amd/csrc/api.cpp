@@ -175,7 +175,7 @@ oq_status oq_rotate_quantize_act(const void* x, oq_dtype x_dtype, int64_t T, int
     }
   }
   oq::RqPlan plan;
-  if (!oq::rq_plan(d, m, x_dtype == OQ_BF16, T, G, &plan))
+  if (!oq::rq_plan(d, m, x_dtype == OQ_BF16, bits_a, T, G, &plan))
     return fail(OQ_EUNSUPPORTED, "no rotate-quantize kernel for d=%d h=%d (d/16 must be a multiple of 64 up to 768, or a power of two below 64)", d, h);
   if (T == 0) return ok();
 

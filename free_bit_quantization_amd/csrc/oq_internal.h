@@ -57,7 +57,7 @@ struct RqPlan {
 };
 
 // Returns false if (d, h) has no kernel.
-bool rq_plan(int32_t d, int32_t log2h, bool bf16, int64_t T, int G, RqPlan* plan);
+bool rq_plan(int32_t d, int32_t log2h, bool bf16, int32_t bits, int64_t T, int G, RqPlan* plan);
 hipError_t rq_launch(const RqArgs& a, bool bf16, int bits, const RqPlan& plan, hipStream_t stream);
 
 // ---- weight quantization (offline, fp64) --------------------------------------

@@ -563,6 +563,15 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
 // and a CU keeps one token row in flight per wavefront.  Sign flips are
 // applied while staging (sign'_perm(i) = sign_i), and only the grid search is
 // built here (the host uses rq_act_kernel when the grid is empty).
+constexpr int kByteCells = 256;
+
+// Grid cell of the cell coordinate xc (see rq_wave_kernel).
+template <bool BYTE>
+__device__ __forceinline__ int grid_cell(float xc, int G) {
+  if constexpr (BYTE) return (int)__builtin_amdgcn_cvt_pk_u8_f32(xc, 0u, 0u);
+  else return (int)__builtin_amdgcn_fmed3f(xc, 0.0f, (float)(G - 1));
+}
+
 struct RqwLayout {
   size_t thr, lut, mtab, atab, wave0, row_bytes, wave_bytes, total;
 };
@@ -572,7 +581,7 @@ __host__ __device__ inline RqwLayout rqw_layout(int d, int log2h, int es, int G,
   const int h = 1 << log2h;
   L.thr = 0;              // thr, then thr_lo
   L.lut = 2 * 256 * 4;
-  L.mtab = L.lut + align16(8 * (size_t)(G > 0 ? G : 1));
+  L.mtab = L.lut + align16(8 * (size_t)(G > kByteCells ? G : kByteCells));   // byte cell indices: 256 cells
   const size_t mwords = es == 2 ? (size_t)d / 2 : (size_t)d;   // sign masks of the source words
   L.atab = L.mtab + align16(4 * mwords);                          // gather offsets, 4 d bytes
   L.wave0 = L.atab + align16(4 * (size_t)d);
@@ -597,6 +606,13 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
   constexpr int NV = BF16 ? 2 : 4;                 // 16-byte loads per 16-coordinate chunk
   constexpr int MW = BF16 ? 8 : 16;                // sign-mask words per chunk
   constexpr int d = 1024 * J;
+  // Up to 64 levels the host's grid has at most 256 cells (the plan takes this
+  // kernel only then), so a cell index is one byte conversion: round to
+  // nearest of the cell coordinate minus 1/2 (floor, or at an exact tie the
+  // cell below, which reaches 0.02 of a cell past its edge), saturated to
+  // [0, 255] (NaN gives 0); cells G .. 255 repeat cell G - 1, whose range is
+  // open above.  With 8-bit codes: clamp to [0, G - 1], then truncate.
+  constexpr bool kByteCell = BITS <= 6;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -648,13 +664,24 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
     const int kk = i & 3, l = (i >> 2) & 63, jq = i >> 8;   // table entry i: ((4 j + q) * 64 + l) * 4 + kk
     pa[k] = i < d ? (int)min((unsigned)a.perm[gin(jq >> 2, l, 4 * (jq & 3) + kk)], (unsigned)(d - 1)) : 0;
   }
+  // the kernel-argument tables too (blockDim >= 256 >= kHostGrid): every set-up
+  // load is issued before the first token's row, so waiting for them does not
+  // wait for the row, which streams in under the table build
+  const float thr_i = tid < nthr ? a.thr[tid] : INFINITY;
+  const float thr_lo_i = tid < nthr ? a.thr_lo[tid] : 0.f;   // fp64 residuals, read by the recheck
+  const bool host_grid = G > 0 && G <= kHostGrid;
+  int2 glut_i = make_int2(0, 0);
+  if (host_grid) {
+    const int c = tid < G ? tid : G - 1;
+    glut_i = make_int2(a.glut[c][0], a.glut[c][1]);
+  }
   __builtin_amdgcn_sched_barrier(0);
   if (gw < T) fetch(gw);
   __builtin_amdgcn_sched_barrier(0);
 
-  for (int i = tid; i < 256; i += blockDim.x) {
-    thr[i] = i < nthr ? a.thr[i] : INFINITY;
-    thr[256 + i] = i < nthr ? a.thr_lo[i] : 0.f;   // fp64 residuals, read by the recheck
+  if (tid < 256) {
+    thr[tid] = thr_i;
+    thr[256 + tid] = thr_lo_i;
   }
   int8_t* sp = reinterpret_cast<int8_t*>(smem + Ly.wave0);   // sign' scratch over the wave buffers
   uint32_t* atab = reinterpret_cast<uint32_t*>(smem + Ly.atab);
@@ -667,13 +694,16 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
     }
   }
   __syncthreads();
-  if (G > 0 && G <= kHostGrid) {
-    for (int c = tid; c < G; c += blockDim.x) lut[c] = make_int2(a.glut[c][0], a.glut[c][1]);   // built on the host
+  const int ncell = kByteCell && G < kByteCells ? kByteCells : G;   // cells G .. ncell - 1 repeat cell G - 1
+  if (host_grid) {
+    // built on the host; thread c holds cell min(c, G - 1)
+    if (tid < ncell) lut[tid] = glut_i;
   } else if (G > 0) {
     const double w = 1.0 / a.g_invw;
-    for (int c = tid; c < G; c += blockDim.x) {
-      const double ulo = c == 0 ? -INFINITY : a.g_lo + (c - 0.02) * w - a.g_rmax;
-      const double uhi = c == G - 1 ? INFINITY : a.g_lo + (c + 1.02) * w + a.g_rmax;
+    for (int c = tid; c < ncell; c += blockDim.x) {
+      const int cc = c < G ? c : G - 1;
+      const double ulo = cc == 0 ? -INFINITY : a.g_lo + (cc - 0.02) * w - a.g_rmax;
+      const double uhi = cc == G - 1 ? INFINITY : a.g_lo + (cc + 1.02) * w + a.g_rmax;
       const int base = count_below_f64(thr, nthr, ulo);
       const float th = (base < nthr && (double)thr[base] <= uhi) ? thr[base] : INFINITY;
       lut[c] = make_int2(__float_as_int(th), base);
@@ -689,7 +719,7 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
 
   const float inv_sqrt_h = (float)(1.0 / sqrt((double)H));
   const float kSqrtH = (float)sqrt((double)H);
-  const float og = (float)(-a.g_lo * a.g_invw);
+  const float og = (float)(-a.g_lo * a.g_invw) - (kByteCell ? 0.5f : 0.0f);
   const float ginvw = (float)a.g_invw;
 
   for (int64_t tok = gw; tok < T; tok += nwaves) {
@@ -808,8 +838,7 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
         int2 e[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-          const int ci = (int)__builtin_amdgcn_fmed3f(fmaf(y[8 * hf + q], cg, og), 0.0f, (float)(G - 1));
-          e[q] = lut[ci];
+          e[q] = lut[grid_cell<kByteCell>(fmaf(y[8 * hf + q], cg, og), G)];
         }
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
@@ -831,8 +860,7 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
         uint32_t flags = 0;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int ci = (int)__builtin_amdgcn_fmed3f(fmaf(y[r], cg, og), 0.0f, (float)(G - 1));
-          const float th = __int_as_float(lut[ci].x);
+          const float th = __int_as_float(lut[grid_cell<kByteCell>(fmaf(y[r], cg, og), G)].x);
           flags |= (fabsf(fmaf(y[r], c, -th)) < radius(th) ? 1u : 0u) << r;
         }
         // the norm again, exactly: fp64 squares of the staged row (sign flips do
@@ -1111,7 +1139,7 @@ hipError_t rqw_dispatch(const RqArgs& a, int bits, const RqPlan& p, hipStream_t 
 
 }  // namespace
 
-bool rq_plan(int32_t d, int32_t log2h, bool bf16, int64_t T, int G, RqPlan* p) {
+bool rq_plan(int32_t d, int32_t log2h, bool bf16, int32_t bits, int64_t T, int G, RqPlan* p) {
   if (log2h < 1 || log2h > 8 || d % 16 != 0 || d % (1 << log2h) != 0) return false;
   const int ns = d / 16;
   p->wave_j = 0;
@@ -1119,7 +1147,8 @@ bool rq_plan(int32_t d, int32_t log2h, bool bf16, int64_t T, int G, RqPlan* p) {
   p->pad = 1;
   // one wavefront per token: d = 1024 J with J <= 5 (bf16) or J <= 2 (fp32: the
   // prefetched row takes twice the registers), h in {64, 256}, grid search
-  if (ns % 64 == 0 && ns / 64 <= (bf16 ? 5 : 2) && (log2h == 6 || log2h == 8) && G > 0) {
+  if (ns % 64 == 0 && ns / 64 <= (bf16 ? 5 : 2) && (log2h == 6 || log2h == 8) && G > 0 &&
+      (bits > 6 || G <= kByteCells)) {
     const int J = ns / 64;
     const int es = bf16 ? 2 : 4;
     // J <= 3: 768 threads, 3 wavefronts per SIMD; J = 4, 5: 512 threads (the
