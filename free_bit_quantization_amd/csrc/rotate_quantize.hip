@@ -593,8 +593,12 @@ __host__ __device__ inline RqwLayout rqw_layout(int d, int log2h, int es, int G,
   return L;
 }
 
-template <int LOG2H, bool BF16, int BITS, int J>
-__global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArgs a, const int WPB) {
+// MAXT: the workgroup size the kernel is built for, 768 (12 wavefronts, 3 per
+// SIMD: at most 170 VGPRs) or 512 (8 wavefronts: 256).  With 768 the slots of a
+// token run one after the other (a rolled loop) so that the live values fit
+// without spilling; with 512 the slot loop is unrolled and its slots overlap.
+template <int LOG2H, bool BF16, int BITS, int J, int MAXT>
+__global__ void __launch_bounds__(MAXT) rq_wave_kernel(const RqArgs a, const int WPB) {
   constexpr int H = 1 << LOG2H;
   constexpr int ES = BF16 ? 2 : 4;
   constexpr int BL = H / 16;                       // lanes per Hadamard block (h >= 32: two passes)
@@ -760,8 +764,7 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
 
     const uint32_t rowbase = (uint32_t)(Ly.wave0 + (size_t)wave * Ly.wave_bytes);
     double inv64 = 0.0;   // 1 / (sqrt(h) (s + eps)) from the exact norm, once a slot needs it
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
+    auto slot = [&](const int j) {
       // ---- 2. gather ---------------------------------------------------------------
       uint32_t addr[16];
 #pragma unroll
@@ -947,6 +950,13 @@ __global__ void __launch_bounds__(J <= 3 ? 768 : 512) rq_wave_kernel(const RqArg
           xr[k] = f32x4{y[4 * k] * inv_sqrt_h, y[4 * k + 1] * inv_sqrt_h, y[4 * k + 2] * inv_sqrt_h,
                         y[4 * k + 3] * inv_sqrt_h};
       }
+    };
+    if constexpr (MAXT > 512) {
+#pragma unroll 1
+      for (int j = 0; j < J; ++j) slot(j);
+    } else {
+#pragma unroll
+      for (int j = 0; j < J; ++j) slot(j);
     }
     if (lane == 0) a.s[tok] = s32;
     wave_sync_lds();  // every lane's gathers are done before the next row is staged
@@ -1088,9 +1098,10 @@ hipError_t rq_dispatch(const RqArgs& a, int bits, const RqPlan& p, hipStream_t s
   }
 }
 
-template <int LOG2H, bool BF16, int BITS, int J>
+template <int LOG2H, bool BF16, int BITS, int J, int MAXT>
 hipError_t rqw_go(const RqArgs& a, const RqPlan& p, hipStream_t st) {
-  auto kern = rq_wave_kernel<LOG2H, BF16, BITS, J>;
+  if (p.threads > MAXT) return hipErrorInvalidValue;
+  auto kern = rq_wave_kernel<LOG2H, BF16, BITS, J, MAXT>;
   hipError_t e = allow_lds(kern);
   int grid = 0;
   if (e == hipSuccess) e = resident_grid(kern, p, &grid);
@@ -1101,17 +1112,20 @@ hipError_t rqw_go(const RqArgs& a, const RqPlan& p, hipStream_t st) {
 
 template <int LOG2H, bool BF16, int BITS>
 hipError_t rqw_dispatch_j(const RqArgs& a, const RqPlan& p, hipStream_t st) {
+  // 12 wavefronts (J <= 3, from 3072 tokens on) or 8
+  const bool big = p.threads > 512;
   switch (p.wave_j) {
-    case 1: return rqw_go<LOG2H, BF16, BITS, 1>(a, p, st);
-    case 2: return rqw_go<LOG2H, BF16, BITS, 2>(a, p, st);
+    case 1: return big ? rqw_go<LOG2H, BF16, BITS, 1, 768>(a, p, st) : rqw_go<LOG2H, BF16, BITS, 1, 512>(a, p, st);
+    case 2: return big ? rqw_go<LOG2H, BF16, BITS, 2, 768>(a, p, st) : rqw_go<LOG2H, BF16, BITS, 2, 512>(a, p, st);
     case 3:
-      if constexpr (BF16) return rqw_go<LOG2H, BF16, BITS, 3>(a, p, st);
+      if constexpr (BF16)
+        return big ? rqw_go<LOG2H, BF16, BITS, 3, 768>(a, p, st) : rqw_go<LOG2H, BF16, BITS, 3, 512>(a, p, st);
       else return hipErrorInvalidValue;
     case 4:
-      if constexpr (BF16) return rqw_go<LOG2H, BF16, BITS, 4>(a, p, st);
+      if constexpr (BF16) return rqw_go<LOG2H, BF16, BITS, 4, 512>(a, p, st);
       else return hipErrorInvalidValue;
     case 5:
-      if constexpr (BF16) return rqw_go<LOG2H, BF16, BITS, 5>(a, p, st);
+      if constexpr (BF16) return rqw_go<LOG2H, BF16, BITS, 5, 512>(a, p, st);
       else return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
