@@ -440,13 +440,17 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
     Pack16<BITS> pk;
     uint32_t flags = 0;
     auto put = [&](int r, int idx) { pk.put(r, (uint32_t)idx); };
-    constexpr bool kSlotRadius = BITS <= 4;
+    // guard radius: the butterfly term of the coordinate's block plus k u
+    // |theta| of the compared threshold, per coordinate, the flags kept as a
+    // bitmask on the fast path (here a slot-wide max |theta| radius with an
+    // any-lane test and recomputed flags measured slower: the workgroup's
+    // wavefronts meet at the next token's barrier, so a recheck anywhere
+    // delays all of them)
     auto radius = [&](int r, float th) {
       const float radb = kGam * l1[TWO_PASS ? 0 : r / (16 / BPL)] * c;
-      return kSlotRadius ? fmaf(a.thr_absmax, kRel, radb) : fmaf(fabsf(th), kRel, radb);
+      return fmaf(fabsf(th), kRel, radb);
     };
     if (G > 0) {
-      bool near = false;
       // two halves of 8: all LUT reads of a half are in flight together
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
@@ -462,15 +466,7 @@ __global__ void __launch_bounds__(768) rq_act_kernel(const RqArgs a, const int N
           const float th = __int_as_float(e[q].x);
           const float dd = fmaf(y[r], c, -th);
           put(r, e[q].y + (dd > 0.f ? 1 : 0));
-          near |= fabsf(dd) < radius(r, th);
-        }
-      }
-      if (__ballot(near && valid) != 0) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ci = (int)__builtin_amdgcn_fmed3f(fmaf(y[r], cg, og), 0.0f, (float)(G - 1));
-          const float th = __int_as_float(lut[ci].x);
-          flags |= (fabsf(fmaf(y[r], c, -th)) < radius(r, th) ? 1u : 0u) << r;
+          flags |= (fabsf(dd) < radius(r, th) ? 1u : 0u) << r;
         }
       }
     } else {
