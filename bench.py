@@ -158,6 +158,11 @@ def measure_linear(lin, index, steps, warmup, ring_mb, dev, split=True):
     ms_step = total_ms / steps
     t_rq = sum(e[0].elapsed_time(e[1]) for e in ev) / steps
     t_ql = sum(e[1].elapsed_time(e[2]) for e in ev) / steps
+    # medians of the per-step intervals (the model card reports warm medians)
+    med = lambda v: sorted(v)[len(v) // 2]
+    medians = {"step": med([e[0].elapsed_time(e[2]) for e in ev]),
+               "rotate_quant": med([e[0].elapsed_time(e[1]) for e in ev]),
+               "qlinear": med([e[1].elapsed_time(e[2]) for e in ev])}
     es = xt.element_size()
     rq_bytes = T * K * es + T * K * lin.bits_a // 8 + 4 * T       # read x, write indices and s
     flops = 2.0 * T * K * N
@@ -165,6 +170,7 @@ def measure_linear(lin, index, steps, warmup, ring_mb, dev, split=True):
              rq_bytes=rq_bytes, flops=flops, rq_gbs=rq_bytes / (t_rq * 1e-3) / 1e9,
              ql_tflops=flops / (t_ql * 1e-3) / 1e12, value=flops / (ms_step * 1e-3) / 1e12,
              entry="oq_qlinear_splitk" if ws is not None else "oq_qlinear", ws_bytes=0 if ws is None else ws.numel(),
+             medians=medians,
              inputs=(x, Wm, perm, sign, c_a, th_a, c_w, th_w))
     return r
 
@@ -405,6 +411,7 @@ def main():
         "qlinear_ms": round(t_ql, 5),
         "rotate_quant_GBps": round(rq_gbs, 1),
         "rotate_quant_ms": round(t_rq, 5),
+        "median_ms": {k: round(v, 5) for k, v in r["medians"].items()},
         "roofline": {"bound": "mfma", "achieved": round(ql_tflops, 2), "peak": FP16_MFMA_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(ql_tflops / FP16_MFMA_PEAK_TFLOPS, 4),
                      "traffic": traffic_of("free_bit_quantization_amd/csrc/qlinear.hip"), "traffic_unit": "bytes",
@@ -417,7 +424,7 @@ def main():
                                   "unit": "GB/s", "frac": round(rq_gbs / HBM_PEAK_GBS, 4),
                                   "traffic": traffic_of("free_bit_quantization_amd/csrc/rotate_quantize.hip"),
                                   "traffic_unit": "bytes", "traffic_source": TRAFFIC_SOURCE,
-                                  "kernel": "oq_rotate_quantize_act (rq_wave_kernel<8,bf16,4,3>)",
+                                  "kernel": "oq_rotate_quantize_act (rq_wave_kernel<8,bf16,4,3,768>)",
                                   "algorithmic": f"T*(K*{es} + K*{lin.bits_a}/8 + 4) = {rq_bytes} B"},
         "wall_s_timed": round(t_wall, 4),
     }
