@@ -13,6 +13,8 @@
 //   6. a workgroup leaves at most one partial (one slot per workgroup), and
 //      computes it before any piece it finishes;
 //   7. the grid fits the workspace's slots.
+// Also simulates the workspace's launch-generation protocol (ql_epoch and
+// friends): `ql_split_check protocol`.
 // Usage: ql_split_check ntiles nst cus [slots]   (one case, the plan's choice)
 //        ql_split_check sweep                      (a broad sweep: the plan, and
 //                                                   the split forced on every tail)
@@ -20,6 +22,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <utility>
 #include <map>
 #include <set>
 #include <vector>
@@ -112,6 +115,80 @@ static int check_split(const QlSplit& p, int64_t ntiles, int nst, int cus, int64
   return 0;
 }
 
+// ---- the launch-generation protocol of a workspace, simulated ------------------------
+// A sequence of split launches on one zero-filled workspace, workgroups
+// starting in a scrambled order.  Launch `poison` loses one producer's flag
+// (its producer never publishes: a device that stopped dispatching); every
+// finisher looks at its contributors' flags before and after this launch's
+// producers publish.  Checks: epochs are never 0 and differ from the previous
+// launch's; before publication no contributor flag is ready (flags left by
+// earlier launches, including the poisoned one, never match); after it all
+// are, except the lost one in the poisoned launch; the header is back to
+// (next generation, 0 started) after each launch.  `gen0` starts the
+// generation near the 32-bit wrap.
+static int protocol(int64_t ntiles, int nst, int cus, uint32_t gen0, int launches, int poison) {
+  const QlSplit p = ql_split_make(ntiles, nst, cus, true);
+  if (p.sk_tiles == 0) return 0;
+  uint32_t hdr[2] = {gen0, 0u};
+  std::vector<uint32_t> flags(p.grid, 0u);
+  uint32_t prev_epoch = 0;
+  uint64_t rng = 0x9E3779B97F4A7C15ull ^ (uint64_t)ntiles;
+  for (int L = 0; L < launches; ++L) {
+    // starts, in a scrambled order: each reads the generation, then counts itself
+    std::vector<int> order(p.grid);
+    for (int b = 0; b < p.grid; ++b) order[b] = b;
+    for (int i = p.grid - 1; i > 0; --i) {
+      rng = rng * 6364136223846793005ull + 1442695040888963407ull;
+      std::swap(order[i], order[(int)((rng >> 33) % (uint64_t)(i + 1))]);
+    }
+    std::vector<uint32_t> epoch(p.grid);
+    for (int b : order) {
+      const uint32_t g = hdr[0];
+      epoch[b] = ql_epoch(g);
+      const uint32_t old = hdr[1]++;
+      if (ql_last_starter(old, (uint32_t)p.grid)) {
+        hdr[1] = 0;
+        hdr[0] = ql_next_gen(g);
+      }
+    }
+    const uint32_t ep = epoch[0];
+    for (int b = 0; b < p.grid; ++b)
+      if (epoch[b] != ep) return fail("epochs differ within a launch", ntiles, nst, cus, cus, L, b);
+    if (ep == 0) return fail("epoch 0", ntiles, nst, cus, cus, L);
+    if (L > 0 && ep == prev_epoch) return fail("epoch repeated", ntiles, nst, cus, cus, L);
+    if (hdr[1] != 0 || hdr[0] != ql_next_gen(ep - 1u)) return fail("header after the starts", ntiles, nst, cus, cus, L);
+    prev_epoch = ep;
+    // producers and finishers of this launch
+    std::vector<int> producers;
+    std::vector<std::vector<int>> waits;   // per finisher, its contributors
+    for (int b = 0; b < p.grid; ++b) {
+      const QlClass c = ql_class(p, b);
+      for (int k = 0; k < ql_npieces(p, c); ++k) {
+        int64_t tl;
+        int s0, s1, role;
+        ql_piece(p, c, k, &tl, &s0, &s1, &role);
+        if (role == 1) producers.push_back(b);
+        if (role == 2) {
+          int cw[4];
+          const int n = ql_contributors(p, c, tl, cw);
+          if (n > 0) waits.push_back(std::vector<int>(cw, cw + n));
+        }
+      }
+    }
+    for (const auto& w : waits)
+      for (int c : w)
+        if (ql_flag_ready(flags[c], ep)) return fail("stale flag ready before publication", ntiles, nst, cus, cus, L, c);
+    const int lost = (L == poison && !producers.empty()) ? producers[producers.size() / 2] : -1;
+    for (int b : producers)
+      if (b != lost) flags[b] = ep;
+    for (const auto& w : waits)
+      for (int c : w)
+        if (ql_flag_ready(flags[c], ep) != (c != lost))
+          return fail("flag readiness after publication", ntiles, nst, cus, cus, L, c);
+  }
+  return 0;
+}
+
 int main(int argc, char** argv) {
   long cases = 0;
   if (argc >= 4) {
@@ -122,6 +199,18 @@ int main(int argc, char** argv) {
     const QlSplit p = ql_split_plan(ntiles, nst, cus, slots);
     std::printf("ok 1 n_dp=%lld sk_tiles=%d grid=%d classes=%d lmin=%d\n", (long long)p.n_dp, p.sk_tiles, p.grid,
                 p.classes, p.lmin);
+    return 0;
+  }
+  if (argc == 2 && std::strcmp(argv[1], "protocol") == 0) {
+    const uint32_t gens[] = {0u, 7u, 0xFFFFFFFCu};
+    for (uint32_t g : gens)
+      for (int64_t nt : {(int64_t)8, (int64_t)36, (int64_t)136 + 512, (int64_t)200, (int64_t)300})
+        for (int nst : {4, 24, 96}) {
+          if (protocol(nt, nst, 256, g, 6, 2)) return 1;
+          if (protocol(nt, nst, 80, g, 6, 0)) return 1;
+          cases += 2;
+        }
+    std::printf("ok %ld\n", cases);
     return 0;
   }
   if (argc == 2 && std::strcmp(argv[1], "sweep") == 0) {

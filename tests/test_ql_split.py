@@ -87,3 +87,9 @@ def test_no_split_without_slots(checker):
 
 def test_sweep_of_tile_counts_stages_and_cu_counts(checker):
     _run(checker, "sweep")
+
+
+def test_launch_generation_protocol(checker):
+    # epoch-tagged flags over a sequence of launches on one workspace, one of
+    # them losing a producer's flag, starting also near the 32-bit wrap
+    _run(checker, "protocol")
