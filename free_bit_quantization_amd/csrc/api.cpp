@@ -267,7 +267,7 @@ oq_status device_cus(int* cus) {
 
 oq::QlSplit qlinear_plan(int64_t T, int32_t d_out, int32_t d_in, int32_t bits_a, int cus, int64_t slots) {
   const int64_t ntiles = ((T + 255) / 256) * (((int64_t)d_out + 255) / 256);
-  return oq::ql_split_plan(ntiles, d_in / oq::ql_stage_k(bits_a), cus, slots);
+  return oq::ql_split_plan(ntiles, d_in / oq::ql_stage_k(bits_a), cus, slots, oq::ql_stage_weight(bits_a));
 }
 
 // Launch with a workspace of `slots` partial-tile slots laid out at ws (ws may

@@ -72,23 +72,32 @@ OQ_HD inline QlSplit ql_split_make(int64_t ntiles, int32_t nst, int32_t cus, boo
   return p;
 }
 
-// When the split pays (measured on MI355X, 256 CUs, with HIP events over
-// whole-tile and split launches of the same shapes): a split tile costs its
-// partial tiles' round trip through memory and a finisher's wait, so it wins
-// when the whole-tile tail would leave most CUs idle.  At 24 stages per tile
-// it won for tails up to ~a quarter of the CUs (+16 % at 36 tiles, +4 % at 24)
-// and lost beyond (-5 % at 104 and 136 tiles, -14 % at 216); at 96 and 192
-// stages it won up to three quarters (+130 % at 24 tiles, +9 % at 144, +2 % at
-// 192) and lost above (-2 % at 216, -4 % at 240).
-OQ_HD inline bool ql_split_pays(int64_t rem, int32_t nst, int32_t cus) {
-  if (rem <= 0 || nst < 4) return false;
-  return rem * 4 <= cus || (nst >= 64 && rem * 4 <= (int64_t)cus * 3);
+// When the split pays, as a cost model fitted to measurements on MI355X (256
+// CUs; HIP events over whole-tile and split launches of the same shapes, one
+// process, alternating order).  A whole-tile tail costs one tile time, nst
+// stages; split, its rem tiles spread over the CUs cost rem / cus of that plus
+// a fixed overhead (partial tiles written and read back at one CU's bandwidth,
+// the finisher's wait, a second pipeline start) of about 15 stages of a 4-bit
+// activation stage (128 K).  So split iff nst w (1 - rem / cus) > 15, with w
+// a stage's cost relative to that one: 100 (percent) for activations of at
+// most 4 bits, 70 for 8-bit (a 64-wide stage) and 105 for 6-bit (64-wide, pair
+// tables with bank conflicts).  Measured gains behind it: 24 stages, tails of
+// 36 and 32 tiles +16 % and +9 %, 104 and 136 tiles -5 % (FLUX QKV whole);
+// 96 stages, 24 to 192 tiles +130 % to +2 %, 216 tiles -2 %; 8-bit
+// activations, 48 stages, 48 tiles +32 %, 128 tiles +2 %, 144 even; 6-bit,
+// 48 stages, 136 tiles +7.5 % (FLUX QKV W6A6).
+OQ_HD inline int32_t ql_stage_weight(int32_t bits_a) { return bits_a == 8 ? 70 : bits_a == 6 ? 105 : 100; }
+
+OQ_HD inline bool ql_split_pays(int64_t rem, int32_t nst, int32_t cus, int32_t w100) {
+  if (rem <= 0 || rem >= cus || nst < 4) return false;
+  return (int64_t)nst * w100 * (cus - rem) > (int64_t)1500 * cus;
 }
 
 // The plan: split the tail when a workspace with at least `slots` partial-tile
 // slots is available (slots >= the workgroup count) and the split pays.
-OQ_HD inline QlSplit ql_split_plan(int64_t ntiles, int32_t nst, int32_t cus, int64_t slots) {
-  return ql_split_make(ntiles, nst, cus, slots >= cus && ql_split_pays(cus > 0 ? ntiles % cus : 0, nst, cus));
+OQ_HD inline QlSplit ql_split_plan(int64_t ntiles, int32_t nst, int32_t cus, int64_t slots, int32_t w100 = 100) {
+  return ql_split_make(ntiles, nst, cus,
+                       slots >= cus && ql_split_pays(cus > 0 ? ntiles % cus : 0, nst, cus, w100));
 }
 
 // ---- whole tiles -----------------------------------------------------------

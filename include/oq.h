@@ -268,14 +268,15 @@ oq_status oq_qlinear_workspace_size(int64_t T, int32_t d_out, int32_t d_in, int3
  * oq_qlinear_splitk -- oq_qlinear (same passages, same result up to fp32
  * summation order, deterministic) with the last, partial round of output
  * tiles split along K: when a launch has a partial last round (or fewer
- * tiles than compute units), its tiles have at least 4 K stages (of 128, or
- * 64 for 6- and 8-bit activations) and that round holds at most a quarter as
- * many tiles as there are compute units (three quarters when a tile has 64
- * stages or more: where the split measured faster than whole tiles), the
- * workgroups cut that round's K stages into equal runs, and the workgroup
- * that holds a tile's last stage adds the fp32 partial tiles the others left
- * in the workspace, in a fixed order, before the epilogue (stream-K).  Other
- * shapes run as oq_qlinear and ignore the workspace.
+ * tiles than compute units) and splitting it is expected to be faster, the
+ * workgroups cut that round's K stages (of 128, or 64 for 6- and 8-bit
+ * activations) into equal runs, and the workgroup that holds a tile's last
+ * stage adds the fp32 partial tiles the others left in the workspace, in a
+ * fixed order, before the epilogue (stream-K).  "Expected faster" is a cost
+ * model fitted to measurements: with nst stages per tile, rem tiles in the
+ * last round and cus compute units, split iff nst * w * (1 - rem / cus) > 15,
+ * w = 1 for activations of at most 4 bits, 0.7 for 8-bit, 1.05 for 6-bit.
+ * Other shapes run as oq_qlinear and ignore the workspace.
  *
  * workspace       : dev, 256-byte aligned, at least the bytes that
  *                   oq_qlinear_workspace_size gives for this shape (NULL / 0

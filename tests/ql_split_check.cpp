@@ -15,7 +15,7 @@
 //   7. the grid fits the workspace's slots.
 // Also simulates the workspace's launch-generation protocol (ql_epoch and
 // friends): `ql_split_check protocol`.
-// Usage: ql_split_check ntiles nst cus [slots]   (one case, the plan's choice)
+// Usage: ql_split_check ntiles nst cus [slots [w100]]   (one case, the plan's choice)
 //        ql_split_check sweep                      (a broad sweep: the plan, and
 //                                                   the split forced on every tail)
 // Prints "ok <cases>" or the first violated invariant, exit status 1.
@@ -40,8 +40,8 @@ static int fail(const char* what, int64_t ntiles, int nst, int cus, int64_t slot
 static int check_split(const QlSplit& p, int64_t ntiles, int nst, int cus, int64_t slots);
 
 // the plan for a workspace of `slots` slots
-static int check(int64_t ntiles, int nst, int cus, int64_t slots) {
-  return check_split(ql_split_plan(ntiles, nst, cus, slots), ntiles, nst, cus, slots);
+static int check(int64_t ntiles, int nst, int cus, int64_t slots, int w100 = 100) {
+  return check_split(ql_split_plan(ntiles, nst, cus, slots, w100), ntiles, nst, cus, slots);
 }
 
 static int check_split(const QlSplit& p, int64_t ntiles, int nst, int cus, int64_t slots) {
@@ -195,8 +195,9 @@ int main(int argc, char** argv) {
     const int64_t ntiles = std::atoll(argv[1]);
     const int nst = std::atoi(argv[2]), cus = std::atoi(argv[3]);
     const int64_t slots = argc >= 5 ? std::atoll(argv[4]) : cus;
-    if (check(ntiles, nst, cus, slots)) return 1;
-    const QlSplit p = ql_split_plan(ntiles, nst, cus, slots);
+    const int w100 = argc >= 6 ? std::atoi(argv[5]) : 100;
+    if (check(ntiles, nst, cus, slots, w100)) return 1;
+    const QlSplit p = ql_split_plan(ntiles, nst, cus, slots, w100);
     std::printf("ok 1 n_dp=%lld sk_tiles=%d grid=%d classes=%d lmin=%d\n", (long long)p.n_dp, p.sk_tiles, p.grid,
                 p.classes, p.lmin);
     return 0;
@@ -219,10 +220,11 @@ int main(int argc, char** argv) {
     for (int cus : cuss)
       for (int nst : nsts)
         for (int64_t nt = 1; nt <= 3 * cus + 9; ++nt) {
-          for (int64_t slots : {(int64_t)0, (int64_t)cus, (int64_t)cus - 1}) {
-            if (check(nt, nst, cus, slots)) return 1;
-            ++cases;
-          }
+          for (int64_t slots : {(int64_t)0, (int64_t)cus, (int64_t)cus - 1})
+            for (int w100 : {70, 100, 105}) {
+              if (check(nt, nst, cus, slots, w100)) return 1;
+              ++cases;
+            }
           // the split mechanism on every tail, whatever the plan would choose
           if (nst >= 2 && nt % cus != 0) {
             if (check_split(ql_split_make(nt, nst, cus, true), nt, nst, cus, cus)) return 1;

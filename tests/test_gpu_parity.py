@@ -258,9 +258,9 @@ def _untouched_tiles_equal(y_split, y_whole, T, N, n_dp):
 
 
 @pytest.mark.parametrize("T,d,d_out,bits_w,bits_a", [(1024, 3072, 3072, 4, 8), (1024, 12288, 3072, 4, 8),
-                                                     (2100, 1024, 300, 4, 4), (1000, 1024, 2000, 2, 4),
-                                                     (512, 1024, 1024, 4, 4),    # 8 tiles: one per class, 4 pieces
-                                                     (2048, 512, 1024, 4, 4),    # 4 K stages per tile
+                                                     (2100, 3072, 300, 4, 4), (1000, 3072, 2000, 2, 4),
+                                                     (512, 3072, 1024, 4, 4),    # 8 tiles: one per class, 4 pieces
+                                                     (1024, 2048, 512, 4, 4),    # 16 K stages per tile
                                                      (1024, 1024, 1024, 6, 6)])  # 6-bit widths (128 x 64 blocks)
 def test_stream_k_split_tiles(T, d, d_out, bits_w, bits_a):
     # fewer tiles than CUs (8 to 48, some ragged): every tile is split by K
@@ -295,19 +295,19 @@ def test_split_workspace_size_and_rejection():
     assert oq.oq_qlinear_workspace_size(4608, 9216, 3072, 4, 4) == 0     # a tail of 136 short tiles: whole
     assert oq.oq_qlinear_workspace_size(256, 256, 256, 4, 4) == 0        # 2 K stages: no split
     assert oq.oq_qlinear_workspace_size(256, 256, 3072, 4, 4) == n       # one tile of 24 stages: split
-    lin = synth.Linear("ws", 512, 1024, 1024, 256, 4, 4, "student_t", "bf16", 10, 30.0, 0.5, 5, 10.0)
+    lin = synth.Linear("ws", 512, 3072, 1024, 256, 4, 4, "student_t", "bf16", 10, 30.0, 0.5, 5, 10.0)
     x, Wm = synth.gen_linear(lin, 1, 0)
     x_idx, s, _ = P.check_activations(x, "bf16", 256, 4, rows=np.arange(4), want_x_rot=False)
     w_idx, w_norm, _ = P.check_weights(Wm, 256, 4)
-    cb = P.library_codebook(1024, 4)
-    need = oq.oq_qlinear_workspace_size(512, 1024, 1024, 4, 4)
+    cb = P.library_codebook(3072, 4)
+    need = oq.oq_qlinear_workspace_size(512, 1024, 3072, 4, 4)
     assert need > 0
     small = torch.zeros(need - 256, dtype=torch.uint8, device="cuda")
     with pytest.raises(oq.OQError) as e:
-        oq.oq_qlinear_splitk(x_idx, s, w_idx, w_norm, 1024, cb.c, 4, cb.c, 4, small)
+        oq.oq_qlinear_splitk(x_idx, s, w_idx, w_norm, 3072, cb.c, 4, cb.c, 4, small)
     assert e.value.status == oq.OQ_EINVAL and "workspace" in str(e.value)
     with pytest.raises(oq.OQError):
-        oq.oq_qlinear_splitk(x_idx, s, w_idx, w_norm, 1024, cb.c, 4, cb.c, 4, None)
+        oq.oq_qlinear_splitk(x_idx, s, w_idx, w_norm, 3072, cb.c, 4, cb.c, 4, None)
     # a shape without a split (2 K stages per tile) ignores the workspace
     g = torch.Generator(device="cuda").manual_seed(3)
     xi2 = torch.randint(0, 256, (300, 128), dtype=torch.uint8, device="cuda", generator=g)

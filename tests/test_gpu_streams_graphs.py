@@ -25,7 +25,7 @@ def _gpu():
     torch.cuda.set_device(0)
 
 
-def _setup(T=520, d=1024, n=777, h=256, seed=0):
+def _setup(T=520, d=3072, n=777, h=256, seed=0):
     from free_bit_quantization_amd import oq
     lin = synth.Linear("g", T, d, n, h, 4, 4, "student_t", "bf16", 10, 30.0, 0.5, 5, 10.0)
     x, W = synth.gen_linear(lin, seed, 0)
@@ -48,7 +48,7 @@ def test_graph_capture_replays_match_eager(split):
     ws_graph = oq.qlinear_workspace(T, n, d, 4, 4) if split else None
     ws_other = oq.qlinear_workspace(T, n, d, 4, 4) if split else None
     if split:
-        assert ws_graph is not None   # 12 tiles: the split is taken
+        assert ws_graph is not None   # 12 tiles of 24 K stages: the split is taken
 
     def step(stream, xi, ss, yy, ws):
         oq.oq_rotate_quantize_act(xt, lin.h, pd, sd, th, 4, x_idx=xi, s=ss, stream=stream)

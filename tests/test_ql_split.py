@@ -55,14 +55,20 @@ SHAPES = [
     (1024, 3072, 9216, 8), (1024, 3072, 3072, 8), (1024, 3072, 12288, 8), (1024, 12288, 3072, 8),
     (1024, 3072, 3072, 8), (1024, 12288, 3072, 8), (2100, 1024, 300, 4), (1000, 1024, 2000, 4),
     (512, 1024, 1024, 4), (2048, 512, 1024, 4), (1024, 1024, 1024, 6), (520, 1024, 777, 4),
+    (2100, 3072, 300, 4), (1000, 3072, 2000, 4), (512, 3072, 1024, 4), (1024, 2048, 512, 4), (520, 3072, 777, 4),
+    (4608, 3072, 9216, 6), (8192, 12288, 3072, 6),
     (700, 3072, 1030, 4),
 ]
+
+
+def _weight(bits_a):
+    return 70 if bits_a == 8 else 105 if bits_a == 6 else 100
 
 
 @pytest.mark.parametrize("T,K,N,bits_a", SHAPES)
 @pytest.mark.parametrize("cus", [256, 304, 80])
 def test_split_of_workload_shapes(checker, T, K, N, bits_a, cus):
-    _run(checker, _tiles(T, N), _stages(K, bits_a), cus)
+    _run(checker, _tiles(T, N), _stages(K, bits_a), cus, cus, _weight(bits_a))
 
 
 def test_plan_follows_the_measured_split_gains(checker):
@@ -78,6 +84,14 @@ def test_plan_follows_the_measured_split_gains(checker):
     assert "n_dp=256 sk_tiles=32 grid=256 classes=8" in out, out
     out = _run(checker, _tiles(4608, 3072), _stages(12288, 4), 256)
     assert "n_dp=216 sk_tiles=0" in out, out
+    # W6A6 FLUX QKV (48 stages of 64, a tail of 136): +7.5 % split; W4A8 8192 x
+    # 3072 -> 3072 (a tail of 128): +2 %; W4A8 1024 x 3072 -> 9216 (144): even, whole
+    out = _run(checker, _tiles(4608, 9216), _stages(3072, 6), 256, 256, _weight(6))
+    assert "n_dp=512 sk_tiles=136" in out, out
+    out = _run(checker, _tiles(8192, 3072), _stages(3072, 8), 256, 256, _weight(8))
+    assert "n_dp=256 sk_tiles=128" in out, out
+    out = _run(checker, _tiles(1024, 9216), _stages(3072, 8), 256, 256, _weight(8))
+    assert "sk_tiles=0" in out, out
 
 
 def test_no_split_without_slots(checker):
