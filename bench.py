@@ -37,8 +37,8 @@ FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, TFLOP/s
 # bench (FETCH_SIZE x 2, WRITE_SIZE x 1: the copy-kernel calibration), valid only
 # for the kernel source they were taken on (sha256 prefix); otherwise null.
 MEASURED_TRAFFIC = {
-    "free_bit_quantization_amd/csrc/qlinear.hip": ("bf92c7b2d7d2b467", 115.06e6, 169.87e6),
-    "free_bit_quantization_amd/csrc/rotate_quantize.hip": ("ed86c48e87215671", 28.68e6, 7.23e6),
+    "free_bit_quantization_amd/csrc/qlinear.hip": ("09155ef1e7909ae4", 113.41e6, 169.91e6),
+    "free_bit_quantization_amd/csrc/rotate_quantize.hip": ("9dfb6acdbef78b69", 28.68e6, 7.23e6),
 }
 
 
