@@ -442,6 +442,21 @@ def test_gelu_epilogue_matches_fp64_gelu_of_the_gpu_output(T, d, n, bits_w, bits
     rel = np.abs(got - g) / np.maximum(np.abs(g), floor)
     P.log(f"[gelu] max relative difference {rel.max():.3e} over {got.size} outputs")
     assert rel.max() <= 1e-6
+    # special and far values through the bias: +-inf, NaN, +-20, +-13.5, +-0
+    special = np.array([np.inf, -np.inf, np.nan, 20.0, -20.0, 13.5, -13.5, 0.0, -0.0], dtype=np.float32)
+    b2 = bias.clone()
+    b2[:special.size] = torch.from_numpy(special).cuda()
+    z0 = P.run_gemm(x_idx[:1], s[:1] * 1e-30, w_idx, w_norm, d, bits_a, bits_w, ca.c, cw.c, bias=b2)
+    z1 = P.run_gemm(x_idx[:1], s[:1] * 1e-30, w_idx, w_norm, d, bits_a, bits_w, ca.c, cw.c, bias=b2,
+                    epilogue=oq.OQ_EPI_GELU_ERF)
+    torch.cuda.synchronize()
+    gz = quant.gelu_erf(z0.cpu().numpy().astype(np.float64))[0, :special.size]
+    gotz = z1.cpu().numpy().astype(np.float64)[0, :special.size]
+    with np.errstate(invalid="ignore"):
+        ok = np.where(np.isfinite(gz), np.abs(gotz - gz) <= 1e-6 * np.maximum(np.abs(gz), 1e-30),
+                      (gotz == gz) | (np.isnan(gotz) & np.isnan(gz)))
+    P.log(f"[gelu] special values {special.tolist()} -> {gotz.tolist()} (fp64 {gz.tolist()})")
+    assert ok.all()
 
 
 # ---- launch geometry: the result does not depend on how the launch is cut --------
