@@ -276,7 +276,7 @@ oq_status qlinear_launch(oq::QlArgs& a, int32_t bits_a, int32_t bits_w, int cus,
                          hipStream_t stream) {
   a.sp = qlinear_plan(a.T, a.N, a.K, bits_a, cus, slots);
   if (a.sp.sk_tiles > 0) {
-    a.hdr = reinterpret_cast<uint32_t*>(ws);
+    a.hdr = reinterpret_cast<uint64_t*>(ws);
     a.flags = reinterpret_cast<uint32_t*>(ws + oq::ql_ws_flags_offset());
     a.slots = reinterpret_cast<float*>(ws + oq::ql_ws_slots_offset(slots));
   }

@@ -92,10 +92,10 @@ struct QlArgs {
   uint16_t tab_w[256];   // fp16 bits of sqrt(K) * c_w
   // Work split over the persistent workgroups (ql_split.h).  With a split
   // tail the workgroups exchange fp32 partial tiles through a workspace: hdr
-  // (launch generation, started-workgroup count), one flag per workgroup and
-  // one 256 x 256 slot per workgroup.
+  // (launch generation and started-workgroup count in one word), one flag per
+  // workgroup and one 256 x 256 slot per workgroup.
   QlSplit sp;
-  uint32_t* hdr;
+  uint64_t* hdr;
   uint32_t* flags;
   float* slots;
 };

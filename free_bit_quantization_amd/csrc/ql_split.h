@@ -194,21 +194,29 @@ OQ_HD inline int ql_contributors(const QlSplit& p, const QlClass& c, int64_t til
 }
 
 // ---- launch generations of a workspace ---------------------------------------------
-// Header word 0 holds the generation g of the next launch (0 in a zero-filled
-// workspace), word 1 counts the workgroups of the current launch that have
-// started.  Every workgroup reads g when it starts; the launch tags its flags
-// with ql_epoch(g); the last workgroup to start resets the count and stores
-// ql_next_gen(g).  Epochs are never 0, so a flag that was never written does
-// not match, and consecutive launches on one workspace use different epochs,
-// so a flag left by an earlier launch (one whose finisher gave up) does not
-// match either: flags need no clearing.
+// The header is one 64-bit word: its low half holds the generation g of the
+// next launch (0 in a zero-filled workspace), its high half counts the
+// workgroups of the current launch that have started.  Every workgroup adds
+// ql_hdr_start() to the word when it starts, one atomic that also returns g;
+// the launch tags its flags with ql_epoch(g); the workgroup whose increment
+// makes the count reach the grid stores ql_hdr_next(g) (next generation, none
+// started).  That store follows every increment of the launch in the word's
+// order of modifications, so no workgroup of the launch sees the next
+// generation, and no fence is needed.  Epochs are never 0, so a flag that
+// was never written does not match, and consecutive launches on one
+// workspace use different epochs, so a flag left by an earlier launch (one
+// whose finisher gave up) does not match either: flags need no clearing.
 OQ_HD constexpr uint32_t ql_epoch(uint32_t g) { return g + 1u; }
 OQ_HD constexpr uint32_t ql_next_gen(uint32_t g) { return g + 1u < 0xFFFFFFFFu ? g + 1u : 0u; }
 OQ_HD constexpr bool ql_last_starter(uint32_t started_before, uint32_t grid) { return started_before + 1u == grid; }
 OQ_HD constexpr bool ql_flag_ready(uint32_t flag, uint32_t epoch) { return flag == epoch; }
+OQ_HD constexpr uint64_t ql_hdr_start() { return 1ull << 32; }
+OQ_HD constexpr uint32_t ql_hdr_gen(uint64_t h) { return (uint32_t)h; }
+OQ_HD constexpr uint32_t ql_hdr_started(uint64_t h) { return (uint32_t)(h >> 32); }
+OQ_HD constexpr uint64_t ql_hdr_next(uint32_t g) { return (uint64_t)ql_next_gen(g); }
 
 // ---- workspace layout ----------------------------------------------------------
-// [0, 256)            header: launch generation, workgroups started in this launch
+// [0, 256)            header: one 64-bit word (launch generation, workgroups started)
 // [256, 256 + F)      one 32-bit flag per workgroup slot (F = slots * 4, rounded up to 256)
 // [256 + F, ...)      slots of 256 x 256 fp32 partial tiles (256 KB each)
 constexpr int64_t kQlSlotBytes = 256 * 256 * 4;

@@ -129,7 +129,7 @@ static int check_split(const QlSplit& p, int64_t ntiles, int nst, int cus, int64
 static int protocol(int64_t ntiles, int nst, int cus, uint32_t gen0, int launches, int poison) {
   const QlSplit p = ql_split_make(ntiles, nst, cus, true);
   if (p.sk_tiles == 0) return 0;
-  uint32_t hdr[2] = {gen0, 0u};
+  uint64_t hdr = gen0;   // generation gen0, none started
   std::vector<uint32_t> flags(p.grid, 0u);
   uint32_t prev_epoch = 0;
   uint64_t rng = 0x9E3779B97F4A7C15ull ^ (uint64_t)ntiles;
@@ -143,20 +143,19 @@ static int protocol(int64_t ntiles, int nst, int cus, uint32_t gen0, int launche
     }
     std::vector<uint32_t> epoch(p.grid);
     for (int b : order) {
-      const uint32_t g = hdr[0];
+      const uint64_t old = hdr;   // the atomic add's result
+      hdr += ql_hdr_start();
+      const uint32_t g = ql_hdr_gen(old);
       epoch[b] = ql_epoch(g);
-      const uint32_t old = hdr[1]++;
-      if (ql_last_starter(old, (uint32_t)p.grid)) {
-        hdr[1] = 0;
-        hdr[0] = ql_next_gen(g);
-      }
+      if (ql_last_starter(ql_hdr_started(old), (uint32_t)p.grid)) hdr = ql_hdr_next(g);
     }
     const uint32_t ep = epoch[0];
     for (int b = 0; b < p.grid; ++b)
       if (epoch[b] != ep) return fail("epochs differ within a launch", ntiles, nst, cus, cus, L, b);
     if (ep == 0) return fail("epoch 0", ntiles, nst, cus, cus, L);
     if (L > 0 && ep == prev_epoch) return fail("epoch repeated", ntiles, nst, cus, cus, L);
-    if (hdr[1] != 0 || hdr[0] != ql_next_gen(ep - 1u)) return fail("header after the starts", ntiles, nst, cus, cus, L);
+    if (ql_hdr_started(hdr) != 0 || ql_hdr_gen(hdr) != ql_next_gen(ep - 1u))
+      return fail("header after the starts", ntiles, nst, cus, cus, L);
     prev_epoch = ep;
     // producers and finishers of this launch
     std::vector<int> producers;
