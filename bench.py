@@ -37,7 +37,7 @@ FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, TFLOP/s
 # bench (FETCH_SIZE x 2, WRITE_SIZE x 1: the copy-kernel calibration), valid only
 # for the kernel source they were taken on (sha256 prefix); otherwise null.
 MEASURED_TRAFFIC = {
-    "free_bit_quantization_amd/csrc/qlinear.hip": ("09155ef1e7909ae4", 113.41e6, 169.91e6),
+    "free_bit_quantization_amd/csrc/qlinear.hip": ("79ccc4d384d96871", 113.53e6, 169.91e6),
     "free_bit_quantization_amd/csrc/rotate_quantize.hip": ("9dfb6acdbef78b69", 28.68e6, 7.23e6),
 }
 
