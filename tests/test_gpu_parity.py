@@ -322,6 +322,41 @@ def test_split_workspace_size_and_rejection():
     assert torch.equal(y, y0)
 
 
+def test_split_launch_generations_across_the_wrap():
+    # The workspace header (one 64-bit word: generation, workgroups started)
+    # set just below the 32-bit wrap: four split launches in a row go through
+    # generations 0xFFFFFFFD, 0xFFFFFFFE, 0 and 1.  After each launch the
+    # header must hold the next generation and a zero count, and y must equal
+    # bit for bit the same launch on a fresh zero-filled workspace (the split's
+    # summation order is fixed, so any stale or missed partial would show).
+    from free_bit_quantization_amd import oq
+    g = torch.Generator(device="cuda").manual_seed(11)
+    T, K, N = 512, 3072, 1024                     # 8 tiles of 24 stages: every tile split
+    x_idx = torch.randint(0, 256, (T, K // 2), dtype=torch.uint8, device="cuda", generator=g)
+    w_idx = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device="cuda", generator=g)
+    s = torch.rand(T, device="cuda", generator=g) + 0.5
+    wn = torch.rand(N, device="cuda", generator=g) + 0.5
+    cb = P.library_codebook(K, 4)
+    ws = oq.qlinear_workspace(T, N, K, 4, 4)
+    assert ws is not None
+    ws[:8].copy_(torch.tensor([0xFFFFFFFD, 0], dtype=torch.int64).to(torch.uint32).view(torch.uint8)[:8])
+
+    def header():
+        h = ws[:8].cpu().view(torch.int32).numpy().view(np.uint32)
+        return int(h[0]), int(h[1])
+
+    assert header() == (0xFFFFFFFD, 0)
+    expect_gen = [0xFFFFFFFE, 0, 1, 2]
+    for k, scale in enumerate((1.0, 1.5, 0.75, 2.0)):
+        y = oq.oq_qlinear_splitk(x_idx, s * scale, w_idx, wn, K, cb.c, 4, cb.c, 4, ws)
+        fresh = oq.qlinear_workspace(T, N, K, 4, 4)
+        y_ref = oq.oq_qlinear_splitk(x_idx, s * scale, w_idx, wn, K, cb.c, 4, cb.c, 4, fresh)
+        torch.cuda.synchronize()
+        assert header() == (expect_gen[k], 0), (k, header())
+        assert bool(torch.isfinite(y).all())
+        assert torch.equal(y, y_ref), k
+
+
 # ---- bf16 output: the fp32 result rounded to nearest even, bit for bit -----------
 
 
