@@ -82,10 +82,11 @@ OQ_HD inline QlSplit ql_split_make(int64_t ntiles, int32_t nst, int32_t cus, boo
 // a stage's cost relative to that one: 100 (percent) for activations of at
 // most 4 bits, 70 for 8-bit (a 64-wide stage) and 105 for 6-bit (64-wide, pair
 // tables with bank conflicts).  Measured gains behind it: 24 stages, tails of
-// 36 and 32 tiles +16 % and +9 %, 104 and 136 tiles -5 % (FLUX QKV whole);
-// 96 stages, 24 to 192 tiles +130 % to +2 %, 216 tiles -2 %; 8-bit
-// activations, 48 stages, 48 tiles +32 %, 128 tiles +2 %, 144 even; 6-bit,
-// 48 stages, 136 tiles +7.5 % (FLUX QKV W6A6).
+// 36, 72, 32 and 28 tiles +35, +6, +12 and +8 %, 132 to 216 tiles -3 to -14 %
+// (136 after two rounds: FLUX QKV, whole); 96 stages, 24 to 192 tiles +150 %
+// to +3 %, 216 tiles -1 %; 8-bit activations, 48 stages, 48 tiles +45 %, 128
+// tiles within 1 %, 144 and 192 tiles -1 and -4 %; 6-bit, 48 stages, 136
+// tiles +8 % (FLUX QKV W6A6).
 OQ_HD inline int32_t ql_stage_weight(int32_t bits_a) { return bits_a == 8 ? 70 : bits_a == 6 ? 105 : 100; }
 
 OQ_HD inline bool ql_split_pays(int64_t rem, int32_t nst, int32_t cus, int32_t w100) {
